@@ -1,0 +1,184 @@
+#!/usr/bin/env python3
+"""Throughput of df11_decode on one MI355X.
+
+One step = one df11_decode launch over a whole transformer block's linear
+weights (one code book, one stream), from DF11 arrays resident in HBM to BF16
+words in HBM.  The default workload is the Llama-3.1-8B-shaped block (q/o
+4096x4096, k/v 1024x4096, gate/up 14336x4096, down 4096x14336; 218,103,808
+weights, N(0, sigma_m) with per-matrix sigma jitter).  R identical encoded
+copies at different addresses are decoded in turn so that the 256 MB
+Infinity Cache cannot hold a step's inputs from the previous use.
+
+Prints one JSON line.  value = effective GB/s = (algorithmic bytes read +
+2n bytes written) / device time of one launch, where the bytes read are the
+code stream (total_bits / 8), the 5-bit gaps, the block positions, the n
+sign|mantissa bytes and the lookup tables.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E peak (vendor figure)
+KERNEL_SOURCE = os.path.join(ROOT, "huffman_decode_amd", "csrc", "df11_decode.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "df11_decode_llama8b_block_traffic.txt")
+
+
+def kernel_hash() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def algorithmic_bytes(enc) -> tuple[int, int]:
+    """(bytes read, bytes written) that DF11 itself must move for one decode."""
+    s = enc.sizes
+    n, nb = int(s.n), int(s.n_blocks)
+    read = (int(s.total_bits) + 7) // 8            # exponent codes
+    read += (5 * (64 * nb + 1) + 7) // 8           # gaps
+    read += 4 * (nb + 1)                            # block output positions
+    read += n                                       # sign|mantissa
+    read += int(s.lut_bytes)                        # tables
+    return read, 2 * n
+
+
+def measured_traffic(n_launch_bytes: int):
+    """HBM bytes per launch from committed rocprofv3 counters, if they were taken
+    on the current kernel source; else None."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    vals = {}
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("kernel_sha256_16") != kernel_hash():
+        return None
+    try:
+        return int(float(vals["hbm_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(wlx, enc) -> dict:
+    """The oracle's serial bit-by-bit decode + join over the whole block, one core."""
+    import numpy as np
+    import oracle
+    n = int(enc.sizes.n)
+    t0 = time.perf_counter()
+    ex, end = oracle.decode(enc.stream, int(enc.sizes.total_bits), 0, n, enc.codebook.lengths)
+    w = oracle.join_bf16(ex, enc.signmant[:n])
+    dt = time.perf_counter() - t0
+    ok = bool(np.array_equal(w, wlx.weights)) and end == int(enc.sizes.total_bits)
+    rd, wr = algorithmic_bytes(enc)
+    return {"value": round((rd + wr) / dt / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "kind": "oracle", "gweights_per_s": round(n / dt / 1e9, 5), "seconds": round(dt, 2),
+            "bit_exact": ok,
+            "sample": f"whole {wlx.name} ({n} weights): oracle serial tree-walk decode "
+                      f"of every code from bit 0, then BF16 join, 1 thread"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="llama8b_block")
+    ap.add_argument("--copies", type=int, default=3,
+                    help="rotating encoded copies (defeats the Infinity Cache)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; the decode shards "
+                                   "without communication (see DESIGN.md), but --gpus must be 1"}))
+        return 2
+
+    import numpy as np
+    import torch
+    import huffman_decode_amd as hd
+    from huffman_decode_amd import workloads as wl
+
+    if not os.path.exists(hd.LIB_PATH):
+        from huffman_decode_amd.build import build_library
+        build_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    t0 = time.perf_counter()
+    wlx = wl.CONFIGS[args.workload]()
+    enc = hd.encode(wlx.weights)
+    t_enc = time.perf_counter() - t0
+    n = enc.n
+    copies = [hd.to_device(enc, dev) for _ in range(max(1, args.copies))]
+    out = torch.empty(n, dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    for k in range(args.warmup):
+        hd.df11_decode(copies[k % len(copies)], out, stream)
+    torch.cuda.synchronize()
+
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for k in range(args.steps):
+        starts[k].record(stream)
+        hd.df11_decode(copies[k % len(copies)], out, stream)
+        ends[k].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+
+    ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    avg_ms = sum(ms) / len(ms)
+    rd, wr = algorithmic_bytes(enc)
+    gbs = (rd + wr) / (avg_ms * 1e-3) / 1e9
+    orig = torch.from_numpy(wlx.weights.view(np.int16)).to(dev)
+    bit_exact = bool(torch.equal(out.view(torch.int16), orig))
+    traffic = measured_traffic(rd + wr)
+
+    line = {
+        "metric": "df11_decode effective HBM GB/s + Gweights/s on 1 MI355X; % of HBM roofline",
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u32",
+        "data": "synthetic",
+        "gweights_per_s": round(n / (avg_ms * 1e-3) / 1e9, 2),
+        "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+        "kernel_ms": {"mean": round(avg_ms, 5), "min": round(min(ms), 5),
+                      "median": round(sorted(ms)[len(ms) // 2], 5)},
+        "bit_exact": bit_exact,
+        "config": {"workload": args.workload, "n_weights": n,
+                   "matrices": [f"{m.name}:{m.rows}x{m.cols}" for m in wlx.matrices],
+                   "bits_per_weight": round(8 * (rd - int(enc.sizes.lut_bytes)) / n, 4),
+                   "total_code_bits": int(enc.sizes.total_bits),
+                   "max_code_len": int(enc.codebook.max_len),
+                   "n_tables": int(enc.codebook.n_tables),
+                   "rotating_copies": len(copies), "host_encode_s": round(t_enc, 2)},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": traffic,
+                     "bytes_per_launch": {"read": rd, "written": wr}},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(wlx, enc)
+    print(json.dumps(line), flush=True)
+    return 0 if bit_exact else 1
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,263 @@
+"""MI355X (gfx950) implementation of the DFloat11 (DF11) decode path.
+
+A thin ctypes binding over ``libdf11.so`` whose C ABI is declared in
+``include/df11.h``.  The functions named ``df11_*`` mirror the C entry points
+one to one and only marshal arguments; every step of encoding runs in the
+library's C++ host code and every step of decoding in its HIP kernel.  PyTorch
+is used only for device memory and streams.
+
+Convenience wrappers: :func:`encode` (host numpy -> :class:`Encoded`),
+:func:`to_device` (-> :class:`DeviceEncoded`) and :func:`decode` (-> a torch
+bfloat16 tensor on the GPU).
+
+Loading fails loudly if the library has not been built
+(``python -m huffman_decode_amd.build``); there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libdf11.so")
+
+DF11_OK = 0
+MAX_CODE_LEN = 32
+BLOCK_BYTES = 512
+STREAM_GUARD = 16
+
+_U8, _U32, _U64, _P = ctypes.c_uint8, ctypes.c_uint32, ctypes.c_uint64, ctypes.c_void_p
+
+
+class Codebook(ctypes.Structure):
+    _fields_ = [("code_len", _U8 * 256), ("code", _U32 * 256), ("max_len", _U32),
+                ("n_symbols", _U32), ("n_tables", _U32), ("lut_bytes", _U32),
+                ("limit_rounds", _U32), ("reserved", _U32)]
+
+    @property
+    def lengths(self) -> np.ndarray:
+        return np.frombuffer(bytes(self.code_len), np.uint8).copy()
+
+    @property
+    def codes(self) -> np.ndarray:
+        return np.array(self.code[:], np.uint32)
+
+
+class Sizes(ctypes.Structure):
+    _fields_ = [("n", _U64), ("total_bits", _U64), ("last_start", _U64), ("stream_bytes", _U64),
+                ("gaps_bytes", _U64), ("block_pos_count", _U64), ("signmant_bytes", _U64),
+                ("lut_bytes", _U64), ("n_blocks", _U32), ("reserved", _U32)]
+
+
+class DeviceStream(ctypes.Structure):
+    _fields_ = [("stream", _P), ("gaps", _P), ("block_pos", _P), ("signmant", _P), ("luts", _P),
+                ("stream_bytes", _U64), ("gaps_bytes", _U64), ("block_pos_count", _U64),
+                ("signmant_bytes", _U64), ("lut_bytes", _U64), ("n", _U64),
+                ("total_bits", _U64), ("last_start", _U64), ("n_blocks", _U32),
+                ("n_tables", _U32), ("status", _P)]
+
+
+class Df11Error(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} failed: {status_string(status)} ({status})")
+        self.status = status
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m huffman_decode_amd.build` (there is no fallback)")
+        lib = ctypes.CDLL(LIB_PATH)
+        lib.df11_status_string.argtypes = [ctypes.c_int]
+        lib.df11_status_string.restype = ctypes.c_char_p
+        lib.df11_histogram.argtypes = [_P, _U64, _P, _U32]
+        lib.df11_build_codebook.argtypes = [_P, _U32, ctypes.POINTER(Codebook)]
+        lib.df11_build_luts.argtypes = [ctypes.POINTER(Codebook), _P, _U64]
+        lib.df11_encoded_sizes.argtypes = [_P, _U64, ctypes.POINTER(Codebook),
+                                           ctypes.POINTER(Sizes)]
+        lib.df11_encode.argtypes = [_P, _U64, ctypes.POINTER(Codebook), _P, _U64, _P, _U64, _P,
+                                    _U64, _P, _U64, ctypes.POINTER(Sizes), _U32]
+        lib.df11_decode.argtypes = [ctypes.POINTER(DeviceStream), _P, _P]
+        for fn in ("df11_histogram", "df11_build_codebook", "df11_build_luts",
+                   "df11_encoded_sizes", "df11_encode", "df11_decode"):
+            getattr(lib, fn).restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def library():
+    """The loaded ctypes library (raises if it is not built)."""
+    return _load()
+
+
+def status_string(status: int) -> str:
+    return _load().df11_status_string(status).decode()
+
+
+def _check(fn: str, status: int) -> None:
+    if status != DF11_OK:
+        raise Df11Error(fn, status)
+
+
+def _ptr(a: np.ndarray) -> int:
+    assert a.flags["C_CONTIGUOUS"]
+    return a.ctypes.data
+
+
+# ------------------------------------------------------------ host entry points
+
+def df11_histogram(bf16: np.ndarray, hist: np.ndarray | None = None, n_threads: int = 0
+                   ) -> np.ndarray:
+    w = np.ascontiguousarray(bf16, dtype=np.uint16).reshape(-1)
+    if hist is None:
+        hist = np.zeros(256, np.uint64)
+    assert hist.dtype == np.uint64 and hist.size == 256 and hist.flags["C_CONTIGUOUS"]
+    _check("df11_histogram", _load().df11_histogram(_ptr(w), w.size, _ptr(hist), n_threads))
+    return hist
+
+
+def df11_build_codebook(hist: np.ndarray, max_code_len: int = MAX_CODE_LEN) -> Codebook:
+    h = np.ascontiguousarray(hist, dtype=np.uint64)
+    cb = Codebook()
+    _check("df11_build_codebook", _load().df11_build_codebook(_ptr(h), max_code_len,
+                                                              ctypes.byref(cb)))
+    return cb
+
+
+def df11_build_luts(cb: Codebook) -> np.ndarray:
+    lut = np.zeros(cb.lut_bytes, np.uint8)
+    _check("df11_build_luts", _load().df11_build_luts(ctypes.byref(cb), _ptr(lut), lut.size))
+    return lut
+
+
+def df11_encoded_sizes(hist: np.ndarray, n: int, cb: Codebook) -> Sizes:
+    h = np.ascontiguousarray(hist, dtype=np.uint64)
+    sz = Sizes()
+    _check("df11_encoded_sizes", _load().df11_encoded_sizes(_ptr(h), n, ctypes.byref(cb),
+                                                            ctypes.byref(sz)))
+    return sz
+
+
+@dataclass
+class Encoded:
+    """Host copy of every DF11 array for one BF16 tensor."""
+    codebook: Codebook
+    sizes: Sizes
+    stream: np.ndarray      # uint8[stream_bytes]
+    gaps: np.ndarray        # uint8[gaps_bytes], packed 5-bit fields
+    block_pos: np.ndarray   # uint32[n_blocks + 1]
+    signmant: np.ndarray    # uint8[signmant_bytes]
+    luts: np.ndarray        # uint8[lut_bytes]
+
+    @property
+    def n(self) -> int:
+        return int(self.sizes.n)
+
+    def compressed_bytes(self) -> int:
+        """Bytes the decoder reads: stream, gaps, block_pos, sign|mantissa, tables."""
+        s = self.sizes
+        return int(s.stream_bytes + s.gaps_bytes + 4 * s.block_pos_count + s.signmant_bytes
+                   + s.lut_bytes)
+
+
+def df11_encode(bf16: np.ndarray, cb: Codebook, hist: np.ndarray | None = None,
+                n_threads: int = 0) -> Encoded:
+    w = np.ascontiguousarray(bf16, dtype=np.uint16).reshape(-1)
+    if hist is None:
+        hist = df11_histogram(w, n_threads=n_threads)
+    sz = df11_encoded_sizes(hist, w.size, cb)
+    stream = np.empty(sz.stream_bytes, np.uint8)
+    gaps = np.empty(sz.gaps_bytes, np.uint8)
+    bp = np.empty(sz.block_pos_count, np.uint32)
+    sm = np.empty(sz.signmant_bytes, np.uint8)
+    out = Sizes()
+    _check("df11_encode", _load().df11_encode(
+        _ptr(w), w.size, ctypes.byref(cb), _ptr(stream), stream.size, _ptr(gaps), gaps.size,
+        _ptr(bp), bp.size, _ptr(sm), sm.size, ctypes.byref(out), n_threads))
+    return Encoded(cb, out, stream, gaps, bp, sm, df11_build_luts(cb))
+
+
+def encode(bf16: np.ndarray, max_code_len: int = MAX_CODE_LEN, n_threads: int = 0) -> Encoded:
+    """Histogram -> code book -> tables -> encoded arrays, all on the host."""
+    w = np.ascontiguousarray(bf16, dtype=np.uint16).reshape(-1)
+    hist = df11_histogram(w, n_threads=n_threads)
+    cb = df11_build_codebook(hist, max_code_len)
+    return df11_encode(w, cb, hist, n_threads)
+
+
+# ------------------------------------------------------------ device side
+
+@dataclass
+class DeviceEncoded:
+    """Device copies of an :class:`Encoded` tensor plus the C descriptor."""
+    desc: DeviceStream
+    tensors: dict
+    n: int
+
+    def compressed_bytes(self) -> int:
+        d = self.desc
+        return int(d.stream_bytes + d.gaps_bytes + 4 * d.block_pos_count + d.signmant_bytes
+                   + d.lut_bytes)
+
+
+def to_device(enc: Encoded, device="cuda", status=None) -> DeviceEncoded:
+    """Copy the encoded arrays to the GPU (torch allocations) and fill a descriptor.
+
+    ``status``: optional int32 device tensor of one element that counts blocks
+    whose decoded symbol count disagrees with block_pos."""
+    import torch
+    t = {
+        "stream": torch.from_numpy(enc.stream).to(device),
+        "gaps": torch.from_numpy(enc.gaps).to(device),
+        "block_pos": torch.from_numpy(enc.block_pos.view(np.int32)).to(device),
+        "signmant": torch.from_numpy(enc.signmant).to(device),
+        "luts": torch.from_numpy(enc.luts).to(device),
+    }
+    if status is not None:
+        t["status"] = status
+    return DeviceEncoded(_descriptor(enc.sizes, enc.codebook.n_tables, t), t, enc.n)
+
+
+def _descriptor(sz: Sizes, n_tables: int, t: dict) -> DeviceStream:
+    d = DeviceStream()
+    d.stream, d.gaps, d.block_pos = t["stream"].data_ptr(), t["gaps"].data_ptr(), \
+        t["block_pos"].data_ptr()
+    d.signmant, d.luts = t["signmant"].data_ptr(), t["luts"].data_ptr()
+    d.stream_bytes = t["stream"].numel()
+    d.gaps_bytes = t["gaps"].numel()
+    d.block_pos_count = t["block_pos"].numel()
+    d.signmant_bytes = t["signmant"].numel()
+    d.lut_bytes = t["luts"].numel()
+    d.n, d.total_bits, d.last_start = sz.n, sz.total_bits, sz.last_start
+    d.n_blocks, d.n_tables = sz.n_blocks, n_tables
+    d.status = t["status"].data_ptr() if "status" in t else None
+    return d
+
+
+def df11_decode(dev: DeviceEncoded, out, stream=None) -> None:
+    """Enqueue the decode of ``dev`` into ``out`` (a CUDA tensor of n bf16/int16
+    elements, 16-byte aligned) on ``stream`` (default: torch's current stream)."""
+    import torch
+    if out.numel() < dev.n or out.element_size() != 2 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous 2-byte tensor with at least n elements")
+    if stream is None:
+        stream = torch.cuda.current_stream(out.device)
+    _check("df11_decode", _load().df11_decode(ctypes.byref(dev.desc), out.data_ptr(),
+                                              stream.cuda_stream))
+
+
+def decode(dev: DeviceEncoded, out=None, stream=None):
+    """Decode into ``out`` (allocated as bfloat16 if None) and return it."""
+    import torch
+    if out is None:
+        out = torch.empty(dev.n, dtype=torch.bfloat16, device=dev.tensors["stream"].device)
+    df11_decode(dev, out, stream)
+    return out

@@ -10,7 +10,10 @@ Llama 3.3 70B, FLUX.1; page "DFloat11: lossless BFloat16 compression", section
 the distributions stated per workload below.
 
 Recipes (numpy PCG64 ``default_rng``; float32 draws rounded to nearest-even BF16;
-row-major ``[out, in]`` matrices concatenated in the listed order):
+row-major ``[out, in]`` matrices concatenated in the listed order).  Each matrix
+is drawn in chunks of 2**22 elements, chunk c of matrix m from
+``default_rng([*seed, m, c])``, so generation runs on several threads and the
+result does not depend on their number:
 
 * ``linear_4096``: one 4096x4096 matrix, N(0, 0.02).
 * ``llama8b_block``: q, k, v, o, gate, up, down of an 8B-class block
@@ -30,9 +33,13 @@ row-major ``[out, in]`` matrices concatenated in the listed order):
 """
 from __future__ import annotations
 
+import os
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field
 
 import numpy as np
+
+CHUNK = 1 << 22
 
 
 def to_bf16(x: np.ndarray) -> np.ndarray:
@@ -41,9 +48,9 @@ def to_bf16(x: np.ndarray) -> np.ndarray:
     NaNs map to a quiet NaN of the same sign (plain RNE on the bit pattern
     would carry a NaN's payload into the exponent or sign)."""
     u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
-    lsb = (u >> np.uint32(16)) & np.uint32(1)
-    rounded = ((u.astype(np.uint64) + np.uint64(0x7FFF) + lsb.astype(np.uint64))
-               >> np.uint64(16)).astype(np.uint16)
+    # only NaN patterns can wrap around 2**32 here; they are replaced below
+    rounded = ((u + (np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))))
+               >> np.uint32(16)).astype(np.uint16)
     nan = np.isnan(x)
     if nan.any():
         rounded[nan] = ((u[nan] >> np.uint32(16)) & np.uint32(0x8000)).astype(np.uint16) | 0x7FC0
@@ -81,14 +88,31 @@ def _layout(shapes: list[tuple[str, int, int]]) -> list[Matrix]:
     return out
 
 
-def _normal_bf16(rng: np.random.Generator, count: int, sigma: float,
-                 out: np.ndarray, chunk: int = 1 << 24) -> None:
+def _threads() -> int:
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def _fill_chunks(out: np.ndarray, seed: list, draw) -> None:
+    """out[c*CHUNK:(c+1)*CHUNK] = to_bf16(draw(default_rng(seed + [c]), size))."""
+    n = out.size
+
+    def one(c):
+        lo, hi = c * CHUNK, min(n, (c + 1) * CHUNK)
+        out[lo:hi] = to_bf16(draw(np.random.default_rng(seed + [c]), hi - lo))
+
+    with ThreadPoolExecutor(_threads()) as ex:
+        list(ex.map(one, range(-(-n // CHUNK))))
+
+
+def _normal_bf16(seed: list, count: int, sigma: float, out: np.ndarray) -> None:
     s = np.float32(sigma)
-    for lo in range(0, count, chunk):
-        hi = min(count, lo + chunk)
-        x = rng.standard_normal(hi - lo, dtype=np.float32)
+
+    def draw(rng, size):
+        x = rng.standard_normal(size, dtype=np.float32)
         x *= s
-        out[lo:hi] = to_bf16(x)
+        return x
+
+    _fill_chunks(out[:count], seed, draw)
 
 
 LLAMA8B_SHAPES = [("q", 4096, 4096), ("k", 1024, 4096), ("v", 1024, 4096), ("o", 4096, 4096),
@@ -109,9 +133,10 @@ def normal_block(name: str, shapes: list[tuple[str, int, int]], seed, sigma: flo
     w = np.empty(total, np.uint16)
     seed = list(seed) if isinstance(seed, (tuple, list)) else [seed]
     for i, m in enumerate(mats):
-        rng = np.random.default_rng(seed + [i])
-        s = sigma * float(2.0 ** rng.uniform(-1.0, 1.0)) if jitter else sigma
-        _normal_bf16(rng, m.numel, s, w[m.offset:m.offset + m.numel])
+        s = sigma
+        if jitter:
+            s = sigma * float(2.0 ** np.random.default_rng(seed + [i]).uniform(-1, 1))
+        _normal_bf16(seed + [i], m.numel, s, w[m.offset:m.offset + m.numel])
     return Workload(name, w, mats)
 
 
@@ -137,13 +162,10 @@ def flux_block(seed: int = 5001, scale: float = 1.0) -> Workload:
     """Heavy-tailed block: 0.02 * Student-t(3) plus 0.01 % large outliers."""
     mats = _layout([(nm, max(1, int(r * scale)), c) for nm, r, c in FLUX_SHAPES])
     total = sum(m.numel for m in mats)
-    rng = np.random.default_rng(seed)
     w = np.empty(total, np.uint16)
-    chunk = 1 << 24
-    for lo in range(0, total, chunk):
-        hi = min(total, lo + chunk)
-        x = rng.standard_t(3.0, hi - lo).astype(np.float32) * np.float32(0.02)
-        w[lo:hi] = to_bf16(x)
+    _fill_chunks(w, [seed, 0],
+                 lambda rng, size: rng.standard_t(3.0, size).astype(np.float32) * np.float32(0.02))
+    rng = np.random.default_rng([seed, 1])
     n_out = int(round(1e-4 * total))
     pos = rng.choice(total, size=n_out, replace=False)
     mag = 10.0 ** rng.uniform(2.0, 4.0, n_out)
@@ -180,9 +202,9 @@ SPECIAL_PATTERNS = [0x0000, 0x8000, 0x0001, 0x807F, 0x007F, 0x7F80, 0xFF80, 0x7F
 def all_exponents(seed: int = 5004, rows: int = 4096, cols: int = 4096) -> Workload:
     """N(0, 0.02) with all 256 exponent values planted at random positions."""
     n = rows * cols
-    rng = np.random.default_rng(seed)
     w = np.empty(n, np.uint16)
-    _normal_bf16(rng, n, 0.02, w)
+    _normal_bf16([seed, 0], n, 0.02, w)
+    rng = np.random.default_rng([seed, 1])
     per = 3
     planted = np.repeat(np.arange(256, dtype=np.uint16), per)
     low = rng.integers(0, 256, planted.size, dtype=np.uint16)

@@ -1,0 +1,129 @@
+"""GPU parity: df11_decode (through the C ABI) against the oracle and the originals.
+
+DF11 is lossless (page "DFloat11: lossless BFloat16 compression", section
+"What it is"), so the decode result is defined as the original BF16 words.
+Every case checks bit-exact equality with them and, where the oracle finishes
+in seconds, element-by-element equality with the oracle's own decode of the
+same seeded input.  Each output buffer is pre-filled with two different
+sentinels on two runs, so an element left unwritten, or written outside the
+tensor, shows up.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import huffman_decode_amd as hd
+from huffman_decode_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+GUARD = 64  # extra output elements past n that must keep their sentinel
+
+
+@pytest.fixture(scope="module")
+def torch():
+    import torch as t
+    if not t.cuda.is_available():
+        pytest.skip("no GPU")
+    return t
+
+
+def _say(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def _gpu_decode(torch, enc, label):
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    dev = hd.to_device(enc, status=st)
+    outs = []
+    for fill in (0x5555, -0x5556):  # 0x5555 and 0xAAAA
+        out = torch.full((enc.n + GUARD,), fill, dtype=torch.int16, device="cuda")
+        _say(f"[gpu] df11_decode {label} n={enc.n} blocks={enc.sizes.n_blocks} "
+             f"tables={enc.codebook.n_tables} max_len={enc.codebook.max_len} fill={fill & 0xFFFF:#x}")
+        hd.df11_decode(dev, out)
+        torch.cuda.synchronize()
+        host = out.cpu().numpy().view(np.uint16)
+        assert (host[enc.n:] == (fill & 0xFFFF)).all(), "write past the end of the tensor"
+        outs.append(host[:enc.n])
+    assert int(st.item()) == 0, "blocks with a count mismatch"
+    assert np.array_equal(outs[0], outs[1])
+    return outs[0]
+
+
+SMALL = [
+    ("n1", lambda: wl.random_small(1, 1, "normal")),
+    ("n2", lambda: wl.random_small(2, 2, "normal")),
+    ("n7", lambda: wl.random_small(7, 3, "normal")),
+    ("n63", lambda: wl.random_small(63, 4, "normal")),
+    ("n64", lambda: wl.random_small(64, 5, "normal")),
+    ("n65", lambda: wl.random_small(65, 6, "normal")),
+    ("n4097", lambda: wl.random_small(4097, 7, "normal")),
+    ("ragged_100003", lambda: wl.random_small(100_003, 8, "normal")),
+    ("ragged_1234567", lambda: wl.random_small(1_234_567, 9, "normal")),
+    ("single_5000", lambda: wl.random_small(5000, 10, "single")),
+    ("single_full_tiles", lambda: wl.random_small(4096 * 70 + 3, 11, "single")),
+    ("uniform_300001", lambda: wl.random_small(300_001, 12, "uniform")),
+    ("int8_200000", lambda: wl.random_small(200_000, 13, "int8")),
+    ("all_exponents_small", lambda: wl.all_exponents(14, 256, 1024).weights),
+    ("flux_small", lambda: wl.flux_block(15, scale=1 / 64).weights),
+]
+
+
+@pytest.mark.parametrize("name,make", SMALL, ids=[s[0] for s in SMALL])
+def test_small_cases_match_oracle(torch, name, make):
+    w = make()
+    enc = hd.encode(w)
+    got = _gpu_decode(torch, enc, name)
+    ref = oracle.encode(w)
+    assert np.array_equal(oracle.decode_tensor(ref), got)  # the oracle's own decode
+    assert np.array_equal(got, w)
+
+
+FULL = ["linear_4096", "fibonacci_33", "fibonacci_34", "all_exponents", "flux_block",
+        "llama8b_block", "llama70b_block"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_configs(torch, name):
+    wlx = wl.CONFIGS[name]()
+    w = wlx.weights
+    enc = hd.encode(w)
+    got = _gpu_decode(torch, enc, name)
+    assert np.array_equal(got, w)
+    # the oracle decodes sampled blocks of the same stream independently
+    rng = np.random.default_rng(99)
+    nb = int(enc.sizes.n_blocks)
+    blocks = np.unique(np.concatenate([[0, nb - 1], rng.choice(nb, min(nb, 48), replace=False)]))
+    stop = int(enc.sizes.last_start) + 1
+    gbits = np.unpackbits(enc.gaps, bitorder="little")
+    for b in blocks.tolist():
+        p0, p1 = int(enc.block_pos[b]), int(enc.block_pos[b + 1])
+        g = 64 * b
+        gap = int(sum(int(gbits[5 * g + j]) << j for j in range(5)))
+        ex = oracle.decode_range(enc.stream, int(enc.sizes.total_bits), 4096 * b + gap,
+                                 min(4096 * (b + 1), stop), enc.codebook.lengths, 4096)
+        assert ex.size == p1 - p0
+        ref = oracle.join_bf16(ex, enc.signmant[p0:p1])
+        assert np.array_equal(got[p0:p1], ref), f"block {b}"
+
+
+def test_gemm_bit_exact_after_decode(torch):
+    """The consumer GEMM sees identical weights: Y = X W^T matches bit for bit."""
+    wlx = wl.linear_4096()
+    enc = hd.encode(wlx.weights)
+    dev = hd.to_device(enc)
+    _say("[gpu] df11_decode linear_4096 for GEMM check")
+    w_dec = hd.decode(dev).view(4096, 4096)
+    w_orig = torch.from_numpy(wlx.weights.view(np.int16)).to("cuda").view(torch.bfloat16)
+    w_orig = w_orig.view(4096, 4096)
+    gen = torch.Generator(device="cuda").manual_seed(3999)
+    for batch in (1, 64):
+        x = torch.randn(batch, 4096, generator=gen, device="cuda").to(torch.bfloat16)
+        y0 = torch.matmul(x, w_orig.t())
+        y0b = torch.matmul(x, w_orig.t())
+        assert torch.equal(y0, y0b), "GEMM itself is not deterministic"
+        y1 = torch.matmul(x, w_dec.t())
+        torch.cuda.synchronize()
+        assert torch.equal(y0, y1)

@@ -1,0 +1,230 @@
+"""Host codec and C-ABI checks that need no GPU.
+
+The host encoder (libdf11) must produce exactly the arrays the oracle computes
+from the format's definitions; its device table image must decode the stream
+when walked the way the kernel walks it (a Python model of one wave, below).
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import huffman_decode_amd as hd
+from huffman_decode_amd import workloads as wl
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _built():
+    if not os.path.exists(hd.LIB_PATH):
+        from huffman_decode_amd.build import build_library
+        build_library()
+    oracle.build()
+
+
+def test_library_exports_every_declared_symbol():
+    text = open(os.path.join(ROOT, "include", "df11.h")).read()
+    declared = set(re.findall(r"\b(df11_\w+)\s*\(", text))
+    assert {"df11_decode", "df11_encode", "df11_build_codebook", "df11_histogram",
+            "df11_encoded_sizes", "df11_build_luts", "df11_status_string"} <= declared
+    lib = ctypes.CDLL(hd.LIB_PATH)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def _inputs():
+    yield "normal_small", wl.random_small(5000, 1, "normal")
+    yield "normal_ragged", wl.random_small(77_777, 2, "normal")
+    yield "single", wl.random_small(3000, 3, "single")
+    yield "uniform", wl.random_small(50_000, 4, "uniform")
+    yield "int8", wl.random_small(40_000, 5, "int8")
+    yield "one", wl.random_small(1, 6, "normal")
+    yield "all_exponents", wl.all_exponents(7, 64, 512).weights
+    yield "flux_small", wl.flux_block(8, scale=1 / 256).weights
+
+
+@pytest.mark.parametrize("name,w", list(_inputs()))
+def test_encode_matches_oracle(name, w):
+    enc = hd.encode(w)
+    ref = oracle.encode(w)
+    cb = enc.codebook
+    assert np.array_equal(cb.lengths, ref.lengths)
+    assert np.array_equal(cb.codes, oracle.canonical_codes(ref.lengths))
+    assert cb.n_tables == oracle.count_subtables(ref.lengths, 8)
+    sz = enc.sizes
+    assert sz.total_bits == ref.total_bits and sz.n_blocks == ref.n_blocks
+    assert np.array_equal(enc.stream, ref.stream)
+    assert np.array_equal(enc.block_pos, ref.block_pos)
+    gaps_ref = oracle.pack_gaps(ref.gaps, enc.gaps.size)
+    assert np.array_equal(enc.gaps, gaps_ref)
+    assert np.array_equal(enc.signmant[:ref.n], ref.signmant)
+    assert not enc.signmant[ref.n:].any()
+    last_len = int(ref.lengths[ref.exponents[-1]])
+    assert sz.last_start == ref.total_bits - last_len
+    # the oracle decodes the product's stream back to the original words
+    ex, end = oracle.decode(enc.stream, int(sz.total_bits), 0, ref.n, cb.lengths)
+    assert end == sz.total_bits
+    assert np.array_equal(oracle.join_bf16(ex, enc.signmant[:ref.n]), w)
+
+
+def test_length_limit_agrees_with_oracle():
+    for k, seed in ((33, 11), (34, 12)):
+        w = wl.fibonacci_exponents(k, seed, 1024, 16384).weights
+        hist = hd.df11_histogram(w)
+        cb = hd.df11_build_codebook(hist, 32)
+        ref, rounds = oracle.limited_lengths(hist, 32)
+        assert np.array_equal(cb.lengths, ref) and cb.limit_rounds == rounds
+        # 33 Fibonacci counts reach exactly 32 bits unlimited; 34 need one halving
+        assert (cb.max_len, cb.limit_rounds) == ((32, 0) if k == 33 else (int(ref.max()), 1))
+
+
+@pytest.mark.parametrize("limit", [8, 10, 12, 16])
+def test_tighter_limits_agree_with_oracle(limit):
+    w = wl.flux_block(21, scale=1 / 128).weights
+    hist = hd.df11_histogram(w)
+    cb = hd.df11_build_codebook(hist, limit)
+    ref, rounds = oracle.limited_lengths(hist, limit)
+    assert np.array_equal(cb.lengths, ref) and cb.limit_rounds == rounds
+
+
+def test_thread_count_does_not_change_output():
+    w = wl.random_small(1_500_001, 9, "normal")
+    a = hd.encode(w, n_threads=1)
+    b = hd.encode(w, n_threads=7)
+    c = hd.encode(w, n_threads=64)
+    for x in (b, c):
+        assert np.array_equal(a.stream, x.stream)
+        assert np.array_equal(a.gaps, x.gaps)
+        assert np.array_equal(a.block_pos, x.block_pos)
+        assert np.array_equal(a.signmant, x.signmant)
+
+
+def test_error_codes():
+    lib = hd.library()
+    hist = np.zeros(256, np.uint64)
+    cb = hd.Codebook()
+    assert lib.df11_build_codebook(hist.ctypes.data, 32, ctypes.byref(cb)) == -1  # empty
+    hist[:] = 1
+    assert lib.df11_build_codebook(hist.ctypes.data, 7, ctypes.byref(cb)) == -3  # 256 syms in 7 bits
+    assert lib.df11_build_codebook(hist.ctypes.data, 33, ctypes.byref(cb)) == -3
+    assert lib.df11_build_codebook(hist.ctypes.data, 8, ctypes.byref(cb)) == 0
+    sz = hd.Sizes()
+    assert lib.df11_encoded_sizes(hist.ctypes.data, 255, ctypes.byref(cb), ctypes.byref(sz)) == -5
+    assert lib.df11_encoded_sizes(hist.ctypes.data, 0, ctypes.byref(cb), ctypes.byref(sz)) == -1
+    # a weight whose exponent has no code
+    w = wl.random_small(1000, 1, "single")
+    cb1 = hd.df11_build_codebook(hd.df11_histogram(w))
+    with pytest.raises(hd.Df11Error):
+        hd.df11_encode(wl.random_small(1000, 2, "normal"), cb1,
+                       hist=hd.df11_histogram(w))
+    # too-small buffers
+    w = wl.random_small(10_000, 3, "normal")
+    h = hd.df11_histogram(w)
+    cb = hd.df11_build_codebook(h)
+    sz = hd.df11_encoded_sizes(h, w.size, cb)
+    buf = np.zeros(sz.stream_bytes, np.uint8)
+    g = np.zeros(sz.gaps_bytes, np.uint8)
+    bp = np.zeros(sz.block_pos_count, np.uint32)
+    sm = np.zeros(sz.signmant_bytes, np.uint8)
+    out = hd.Sizes()
+    st = lib.df11_encode(w.ctypes.data, w.size, ctypes.byref(cb), buf.ctypes.data, buf.size - 1,
+                         g.ctypes.data, g.size, bp.ctypes.data, bp.size, sm.ctypes.data, sm.size,
+                         ctypes.byref(out), 0)
+    assert st == -2
+    # decode descriptor checks happen before any device call
+    d = hd.DeviceStream()
+    assert lib.df11_decode(ctypes.byref(d), None, None) == -1
+    assert lib.df11_decode(None, None, None) == -1
+
+
+def test_decode_rejects_inconsistent_descriptor_on_host():
+    lib = hd.library()
+    w = wl.random_small(10_000, 3, "normal")
+    enc = hd.encode(w)
+    sz = enc.sizes
+    d = hd.DeviceStream()
+    fake = 1 << 20  # aligned non-null addresses; the checks fail before any use
+    d.stream = d.gaps = d.block_pos = d.signmant = d.luts = fake
+    d.stream_bytes, d.gaps_bytes = sz.stream_bytes, sz.gaps_bytes
+    d.block_pos_count, d.signmant_bytes, d.lut_bytes = sz.block_pos_count, sz.signmant_bytes, \
+        sz.lut_bytes
+    d.n, d.total_bits, d.last_start = sz.n, sz.total_bits, sz.last_start
+    d.n_blocks, d.n_tables = sz.n_blocks, enc.codebook.n_tables
+    for field, value, want in (("n_blocks", sz.n_blocks + 1, -5), ("total_bits", sz.n - 1, -5),
+                               ("last_start", sz.total_bits, -5), ("stream_bytes", 100, -2),
+                               ("gaps_bytes", 8, -2), ("n_tables", 0, -4),
+                               ("n_tables", 65, -4), ("n", 0, -1)):
+        saved = getattr(d, field)
+        setattr(d, field, value)
+        assert lib.df11_decode(ctypes.byref(d), fake, None) == want, field
+        setattr(d, field, saved)
+    assert lib.df11_decode(ctypes.byref(d), fake + 2, None) == -1  # misaligned output
+
+
+# ---------------------------------------------------------------------------
+# A Python model of one wave of the decode kernel: per lane, codes that start
+# in [gap, min(64, stop - 64g)) of its slice, read from LSB-first windows via
+# the table image; wave prefix sum; merge into BF16.  It checks the table
+# image and the slice/limit arithmetic the kernel relies on.
+
+@pytest.mark.parametrize("name,w", [
+    ("normal", wl.random_small(9000, 31, "normal")),
+    ("single", wl.random_small(700, 32, "single")),
+    ("uniform", wl.random_small(1500, 33, "uniform")),
+])
+def test_kernel_model_decodes_table_image(name, w):
+    enc = hd.encode(w)
+    got = _model_blocks(enc, range(int(enc.sizes.n_blocks)))
+    assert np.array_equal(np.concatenate([got[b] for b in sorted(got)]), w)
+
+
+@pytest.mark.parametrize("k", [33, 34])
+def test_kernel_model_on_longest_codes(k):
+    """Blocks holding the longest codes (32 bits for 33 Fibonacci counts)."""
+    w = wl.fibonacci_exponents(k, 40 + k, 1024, 16384).weights
+    enc = hd.encode(w)
+    e, _ = oracle.split_bf16(w)
+    ln = enc.codebook.lengths
+    idx = np.nonzero(ln[e] == ln.max())[0][:4]
+    starts = np.concatenate([[0], np.cumsum(ln[e].astype(np.int64))])
+    blocks = sorted({int(starts[i]) // 4096 for i in idx} | {int(enc.sizes.n_blocks) - 1})
+    got = _model_blocks(enc, blocks)
+    for b, vals in got.items():
+        p0, p1 = int(enc.block_pos[b]), int(enc.block_pos[b + 1])
+        assert np.array_equal(vals, w[p0:p1])
+
+
+def _model_blocks(enc, blocks):
+    s = enc.sizes
+    lut = enc.luts.view(np.uint16)
+    bits = np.unpackbits(enc.stream, bitorder="little")
+    gaps_bits = np.unpackbits(enc.gaps, bitorder="little")
+    stop = int(s.last_start) + 1
+    res = {}
+    for b in blocks:
+        syms = []
+        for lane in range(64):
+            g = 64 * b + lane
+            gap = int(sum(int(gaps_bits[5 * g + j]) << j for j in range(5)))
+            lim = max(0, min(64, stop - 64 * g))
+            pos = gap
+            while pos < lim:
+                p = 64 * g + pos
+                w = int(sum(int(bits[p + j]) << j for j in range(32)))
+                e = int(lut[w & 0xFF])
+                lvl = 1
+                while e & 0x8000 and lvl < 4:
+                    e = int(lut[(e & 63) * 256 + ((w >> (8 * lvl)) & 0xFF)])
+                    lvl += 1
+                syms.append(e & 0xFF)
+                pos += ((e >> 8) & 31) + 1
+        p0, p1 = int(enc.block_pos[b]), int(enc.block_pos[b + 1])
+        assert len(syms) == p1 - p0
+        ex = np.array(syms, np.uint16)
+        smb = enc.signmant[p0:p1].astype(np.uint16)
+        res[b] = ((smb & 0x80) << 8) | (ex << 7) | (smb & 0x7F)
+    return res
