@@ -57,7 +57,7 @@ class DeviceStream(ctypes.Structure):
                 ("stream_bytes", _U64), ("gaps_bytes", _U64), ("block_pos_count", _U64),
                 ("signmant_bytes", _U64), ("lut_bytes", _U64), ("n", _U64),
                 ("total_bits", _U64), ("last_start", _U64), ("n_blocks", _U32),
-                ("n_tables", _U32), ("status", _P)]
+                ("n_tables", _U32), ("max_len", _U32), ("reserved", _U32), ("status", _P)]
 
 
 class Df11Error(RuntimeError):
@@ -223,10 +223,10 @@ def to_device(enc: Encoded, device="cuda", status=None) -> DeviceEncoded:
     }
     if status is not None:
         t["status"] = status
-    return DeviceEncoded(_descriptor(enc.sizes, enc.codebook.n_tables, t), t, enc.n)
+    return DeviceEncoded(_descriptor(enc.sizes, enc.codebook, t), t, enc.n)
 
 
-def _descriptor(sz: Sizes, n_tables: int, t: dict) -> DeviceStream:
+def _descriptor(sz: Sizes, cb: Codebook, t: dict) -> DeviceStream:
     d = DeviceStream()
     d.stream, d.gaps, d.block_pos = t["stream"].data_ptr(), t["gaps"].data_ptr(), \
         t["block_pos"].data_ptr()
@@ -237,7 +237,7 @@ def _descriptor(sz: Sizes, n_tables: int, t: dict) -> DeviceStream:
     d.signmant_bytes = t["signmant"].numel()
     d.lut_bytes = t["luts"].numel()
     d.n, d.total_bits, d.last_start = sz.n, sz.total_bits, sz.last_start
-    d.n_blocks, d.n_tables = sz.n_blocks, n_tables
+    d.n_blocks, d.n_tables, d.max_len = sz.n_blocks, cb.n_tables, cb.max_len
     d.status = t["status"].data_ptr() if "status" in t else None
     return d
 

@@ -144,6 +144,8 @@ typedef struct df11_device_stream {
     uint64_t stream_bytes, gaps_bytes, block_pos_count, signmant_bytes, lut_bytes;
     uint64_t n, total_bits, last_start;
     uint32_t n_blocks, n_tables;
+    uint32_t max_len;  /* longest code of the code book (1..32) */
+    uint32_t reserved;
     uint32_t *status;  /* optional device word; each block whose decoded
                           count differs from its block_pos range, or whose
                           block_pos range is malformed, adds 1 (the block's

@@ -153,8 +153,8 @@ def test_decode_rejects_inconsistent_descriptor_on_host():
     d.block_pos_count, d.signmant_bytes, d.lut_bytes = sz.block_pos_count, sz.signmant_bytes, \
         sz.lut_bytes
     d.n, d.total_bits, d.last_start = sz.n, sz.total_bits, sz.last_start
-    d.n_blocks, d.n_tables = sz.n_blocks, enc.codebook.n_tables
-    for field, value, want in (("n_blocks", sz.n_blocks + 1, -5), ("total_bits", sz.n - 1, -5),
+    d.n_blocks, d.n_tables, d.max_len = sz.n_blocks, enc.codebook.n_tables, enc.codebook.max_len
+    for field, value, want in (("max_len", 0, -5), ("max_len", 33, -5), ("n_blocks", sz.n_blocks + 1, -5), ("total_bits", sz.n - 1, -5),
                                ("last_start", sz.total_bits, -5), ("stream_bytes", 100, -2),
                                ("gaps_bytes", 8, -2), ("n_tables", 0, -4),
                                ("n_tables", 65, -4), ("n", 0, -1)):
