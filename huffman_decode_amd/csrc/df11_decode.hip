@@ -18,7 +18,8 @@
 //      count table  : bits taken by all codes that end inside the W bits, and
 //                     their number (phase 1 counts ~4 codes per lookup);
 //      decode table : the first (up to 4) of those symbols, bits and count
-//                     (phase 2 emits up to 4 exponents per lookup);
+//                     (phase 2 stores up to 4 exponents per lookup with one
+//                     4-byte LDS store; ROCm runs gfx9 LDS in unaligned mode);
 //    codes longer than W fall back to the 8-bit tables;
 //  * a lane's 96 relevant stream bits live in three VGPRs; windows come from
 //    one funnel shift (v_alignbit) of a dword pair, with the data pre-shifted
@@ -44,23 +45,43 @@
 
 namespace {
 
+#ifndef DF11_WAVES_PER_GROUP
+#define DF11_WAVES_PER_GROUP 8
+#endif
+#ifndef DF11_COUNT_BITS
+#define DF11_COUNT_BITS 11
+#endif
+#ifndef DF11_DECODE_BITS
+#define DF11_DECODE_BITS 11
+#endif
+
 constexpr int kWave = 64;
-constexpr int kWavesPerGroup = 4;
+constexpr int kWavesPerGroup = DF11_WAVES_PER_GROUP;
 constexpr int kGroupThreads = kWave * kWavesPerGroup;
+#ifndef DF11_TILE_SYMBOLS
+#define DF11_TILE_SYMBOLS 2048
+#endif
 constexpr int kMaxBlockCodes = DF11_BLOCK_SLICES * DF11_SLICE_BITS;  // all 1-bit codes
-constexpr int kTileBytes = kMaxBlockCodes + 16;
+// exponent bytes one tile holds; blocks with more symbols take several passes
+constexpr int kTileCap = DF11_TILE_SYMBOLS;
+constexpr int kTileBytes = kTileCap + 16;
+static_assert(kTileCap % 8 == 0, "tile windows must stay 8-aligned");
 constexpr int kTableBytes = 256 * 2;
 constexpr int kXcds = 8;
 
 // multi-code tables (LDS): window widths
-constexpr int kCountBits = 11;
-constexpr int kDecodeBits = 11;
+constexpr int kCountBits = DF11_COUNT_BITS;
+constexpr int kDecodeBits = DF11_DECODE_BITS;
 constexpr int kCountBytes = (1 << kCountBits) * 4;
 constexpr int kDecodeBytes = (1 << kDecodeBits) * 8;
 constexpr int kMaxSymbolsPerStep = 4;
+constexpr int kTilesBytes = kWavesPerGroup * kTileBytes;
+constexpr int kStaticLds = kTilesBytes + kCountBytes + kDecodeBytes;
+static_assert(kTilesBytes < 0x10000, "tile addresses must fit 16 bits");
 constexpr int kPrefetchGroups = 4;  // sign|mantissa groups of 8 per lane loaded up front
 
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
+typedef __attribute__((address_space(3))) uint32_t lds_u32;
 
 __device__ __forceinline__ uint32_t lds_offset(const void *p) {
     // low 32 bits of a flat address inside the LDS aperture are the LDS offset
@@ -112,18 +133,14 @@ __device__ void build_fast_tables(const uint16_t *lut, uint32_t *count_t, uint2 
         // codes of the bit pattern i (first stream bit in bit 0; zeros past
         // the table width never complete a code that is counted)
         uint32_t pos = 0, k = 0, cpos = 0, ck = 0, dpos = 0, dk = 0;
-        uint32_t s01 = 0, s23 = 0;
+        uint32_t s0123 = 0;
         for (uint32_t step = 0; step < kSpan; ++step) {
             const uint32_t e = lookup8(lut, (uint32_t)i >> pos, n_tables);
             const uint32_t len = leaf_len(e);
             if (pos + len > kSpan) break;
             if (pos + len <= count_w) cpos = pos + len, ck = k + 1;
             if (pos + len <= (uint32_t)kDecodeBits && k < (uint32_t)kMaxSymbolsPerStep) {
-                const uint32_t sym = e & 0xFFu;
-                if (k == 0) s01 |= sym;
-                if (k == 1) s01 |= sym << 16;
-                if (k == 2) s23 |= sym;
-                if (k == 3) s23 |= sym << 16;
+                s0123 |= (e & 0xFFu) << (8 * k);
                 dpos = pos + len;
                 dk = k + 1;
             }
@@ -131,8 +148,9 @@ __device__ void build_fast_tables(const uint16_t *lut, uint32_t *count_t, uint2 
             ++k;
         }
         if (i < (1 << kCountBits)) count_t[i] = cpos | (ck << 16);
-        if (i < (1 << kDecodeBits))
-            dec_t[i] = make_uint2(s01 | (dpos << 8) | (dk << 24), s23);
+        // decode entry: bits | count << 16 (added to the accumulator as is),
+        // then the symbols packed one per byte
+        if (i < (1 << kDecodeBits)) dec_t[i] = make_uint2(dpos | (dk << 16), s0123);
     }
 }
 
@@ -154,6 +172,19 @@ __device__ __forceinline__ uint4 join8(uint2 e, uint2 s) {
     return o;
 }
 
+// Inclusive prefix sum over the 64 lanes with DPP row shifts and row
+// broadcasts (no LDS round trip): rows of 16 first, then row 0's total into
+// row 1 and row 2's into row 3, then lane 31's total into rows 2 and 3.
+__device__ __forceinline__ uint32_t wave_inclusive_sum(uint32_t v) {
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, false);  // row_shr:1
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, false);  // row_shr:2
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, false);  // row_shr:4
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, false);  // row_shr:8
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false);  // row_bcast:15
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false);  // row_bcast:31
+    return v;
+}
+
 __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -168,16 +199,156 @@ __device__ __forceinline__ uint32_t pad_ones(uint32_t d, int end, int base) {
     return d | (0xFFFFFFFFu << keep);
 }
 
+// Phase 1 for one lane: number of codes starting in [pos, stop) of its slice.
+// f* are the slice's dwords with the bits after its last code set to 1,
+// d* the plain dwords (for codes longer than the count window).
+__device__ __forceinline__ uint32_t count_codes(const uint8_t *lds_count, const uint16_t *lut,
+                                                uint32_t n_tables, uint32_t d0, uint32_t d1,
+                                                uint32_t d2, uint32_t f0, uint32_t f1, uint32_t f2,
+                                                uint32_t pos, uint32_t stop) {
+    // pre-shift by 2: window bits [2, 2+W) are the entry's byte offset
+    const uint32_t c0 = f0 << 2, c1 = __builtin_amdgcn_alignbit(f1, f0, 30),
+                   c2 = __builtin_amdgcn_alignbit(f2, f1, 30);
+    constexpr uint32_t kMask = ((1u << kCountBits) - 1) << 2;
+    uint32_t acc = pos;  // pos | count << 16
+    const uint32_t stop0 = stop < 32u ? stop : 32u;
+    // a half holds at most 32 code starts: the bound only matters for corrupt input
+    for (int it = 0; it < 32 && (acc & 0xFFFFu) < stop0; ++it) {
+        const uint32_t w = __builtin_amdgcn_alignbit(c1, c0, acc);
+        uint32_t x = *reinterpret_cast<const uint32_t *>(lds_count + (w & kMask));
+        if (x < 0x10000u)
+            x = leaf_len(lookup8(lut, __builtin_amdgcn_alignbit(d1, d0, acc), n_tables)) | 0x10000u;
+        acc += x;
+    }
+    for (int it = 0; it < 32 && (acc & 0xFFFFu) < stop; ++it) {
+        const uint32_t w = __builtin_amdgcn_alignbit(c2, c1, acc);
+        uint32_t x = *reinterpret_cast<const uint32_t *>(lds_count + (w & kMask));
+        if (x < 0x10000u)
+            x = leaf_len(lookup8(lut, __builtin_amdgcn_alignbit(d2, d1, acc), n_tables)) | 0x10000u;
+        acc += x;
+    }
+    return acc >> 16;
+}
+
+// Phase 2 for one lane: decode the codes starting in [pos, stop) and store
+// their exponent bytes from tile position `at` on (a tile position is the
+// output index minus the block's 8-aligned base).
+//
+// Unranged (the block fits one tile): every lookup stores all four slots of
+// its decode entry.  A slot past the entry's complete codes holds a stray
+// byte, but the lane's next step starts storing exactly there; only the
+// lane's last step can leave stray bytes behind, and at most 3 of them, all
+// on the following lanes' first 3 positions.  Symbols decoded past the
+// lane's own codes are the true next symbols (the bits are real), so they
+// are harmless.  rewrite_head() then restores every lane's first symbols.
+// With kRanged only positions in [r0, r0 + kTileCap) are stored, at
+// tile[position - r0], one checked slot at a time.
+template <bool kRanged>
+__device__ __forceinline__ void decode_codes(const uint8_t *lds_dec, const uint16_t *lut,
+                                             uint32_t n_tables, uint32_t d0, uint32_t d1,
+                                             uint32_t d2, uint32_t pos, uint32_t stop,
+                                             uint32_t tile_addr, uint32_t at, uint32_t r0) {
+    const uint32_t e0 = d0 << 3, e1 = __builtin_amdgcn_alignbit(d1, d0, 29),
+                   e2 = __builtin_amdgcn_alignbit(d2, d1, 29);
+    constexpr uint32_t kMask = ((1u << kDecodeBits) - 1) << 3;
+    // pos | (LDS address of the next exponent byte) << 16; ranged: position << 16
+    uint32_t acc = pos | ((kRanged ? at : tile_addr + at) << 16);
+    const uint32_t stop0 = stop < 32u ? stop : 32u;
+    auto step = [&](uint32_t hi, uint32_t lo, uint32_t dhi, uint32_t dlo) {
+        const uint32_t w = __builtin_amdgcn_alignbit(hi, lo, acc);
+        const uint2 dv = *reinterpret_cast<const uint2 *>(lds_dec + (w & kMask));
+        if (!kRanged) {
+            // all four symbol bytes in one (possibly unaligned) LDS store; a
+            // code longer than the table's window then overwrites byte 0
+            const uint32_t at_lds = acc >> 16;
+            *(lds_u32 *)(uintptr_t)at_lds = dv.y;
+            uint32_t inc = dv.x;
+            if (dv.x < 0x10000u) {
+                const uint32_t e = lookup8(lut, __builtin_amdgcn_alignbit(dhi, dlo, acc), n_tables);
+                *(lds_u8 *)(uintptr_t)at_lds = (uint8_t)e;
+                inc = leaf_len(e) | 0x10000u;
+            }
+            acc += inc;
+        } else {
+            uint32_t syms, k;
+            if (dv.x < 0x10000u) {
+                const uint32_t e = lookup8(lut, __builtin_amdgcn_alignbit(dhi, dlo, acc), n_tables);
+                syms = e & 0xFFu;
+                k = 1;
+                acc += leaf_len(e) | 0x10000u;
+            } else {
+                syms = dv.y;
+                k = dv.x >> 16;
+                acc += dv.x;
+            }
+            const uint32_t p = (acc >> 16) - k;  // position of the first symbol
+            for (uint32_t j = 0; j < 4; ++j) {
+                const uint32_t rel = p + j - r0;
+                if (j < k && rel < (uint32_t)kTileCap)
+                    *((lds_u8 *)(uintptr_t)(tile_addr + rel)) = (uint8_t)(syms >> (8 * j));
+            }
+        }
+    };
+    for (int it = 0; it < 32 && (acc & 0xFFFFu) < stop0; ++it) step(e1, e0, d1, d0);
+    for (int it = 0; it < 32 && (acc & 0xFFFFu) < stop; ++it) step(e2, e1, d2, d1);
+}
+
+// After every lane's unranged decode: store this lane's first min(3, cnt)
+// symbols again (the previous lanes' last steps may have overwritten them).
+// Runs after the loops of all lanes, so these stores land last.
+__device__ __forceinline__ void rewrite_head(const uint8_t *lds_dec, const uint16_t *lut,
+                                             uint32_t n_tables, uint32_t d0, uint32_t d1,
+                                             uint32_t d2, uint32_t pos, uint32_t cnt,
+                                             uint32_t addr) {
+    constexpr uint32_t kMask = ((1u << kDecodeBits) - 1) << 3;
+    const uint32_t need = cnt < 3u ? cnt : 3u;
+    uint32_t done = 0;
+    for (int it = 0; it < 3 && done < need; ++it) {
+        const bool second = pos >= 32;  // codes start below bit 64 of the slice
+        const uint32_t lo = second ? d1 : d0, hi = second ? d2 : d1;
+        const uint32_t wd = __builtin_amdgcn_alignbit(hi, lo, pos);  // plain window
+        const uint2 dv = *reinterpret_cast<const uint2 *>(lds_dec + ((wd << 3) & kMask));
+        lds_u8 *o = (lds_u8 *)(uintptr_t)(addr + done);
+        uint32_t k, b, syms;
+        if (dv.x < 0x10000u) {
+            const uint32_t e = lookup8(lut, wd, n_tables);
+            syms = e & 0xFFu;
+            k = 1;
+            b = leaf_len(e);
+        } else {
+            syms = dv.y;
+            k = dv.x >> 16;
+            b = dv.x & 0xFFFFu;
+        }
+        for (uint32_t j = 0; j < 3; ++j)
+            if (j < k && done + j < need) o[j] = (uint8_t)(syms >> (8 * j));
+        done += k;
+        pos += b;
+    }
+}
+
+// One BF16 word from an exponent byte and a sign|mantissa byte.
+__device__ __forceinline__ uint32_t join1(uint32_t e, uint32_t sm) {
+    return ((sm & 0x80u) << 8) | ((e & 0xFFu) << 7) | (sm & 0x7Fu);
+}
+
 __global__ __launch_bounds__(kGroupThreads) void df11_decode_kernel(DecodeArgs a) {
-    // LDS: count table | decode table (fixed offsets, folded into the
-    // ds_read immediates) | 8-bit tables | per-wave exponent tiles
-    __shared__ uint32_t count_t[1 << kCountBits];
-    __shared__ uint2 dec_t[1 << kDecodeBits];
+    // LDS: per-wave exponent tiles | count table | decode table in one static
+    // array (fixed offsets fold into the ds_read/ds_write immediates, and the
+    // tiles sit at the lowest addresses so a tile address fits the 16-bit field
+    // of the phase-2 accumulator), then the 8-bit tables in dynamic LDS.
+    __shared__ __attribute__((aligned(16))) uint8_t lds_static[kStaticLds];
+    uint8_t *tiles = lds_static;
+    uint32_t *count_t = reinterpret_cast<uint32_t *>(lds_static + kTilesBytes);
+    uint2 *dec_t = reinterpret_cast<uint2 *>(lds_static + kTilesBytes + kCountBytes);
     extern __shared__ uint4 smem_u4[];
-    uint8_t *smem = reinterpret_cast<uint8_t *>(smem_u4);
-    uint16_t *lut = reinterpret_cast<uint16_t *>(smem);
+    uint16_t *lut = reinterpret_cast<uint16_t *>(smem_u4);
     const uint32_t hier_bytes = a.n_tables * kTableBytes;
-    uint8_t *tiles = smem + hier_bytes;
+    if (lds_offset(tiles) + kTilesBytes > 0x10000u) {
+        // tile addresses would not fit the accumulator: decode nothing
+        if (threadIdx.x == 0 && a.status) atomicAdd(a.status, 1u);
+        return;
+    }
 
     uint4 *lut_u4 = reinterpret_cast<uint4 *>(lut);
     for (uint32_t i = threadIdx.x; i < hier_bytes / 16; i += kGroupThreads) lut_u4[i] = a.luts[i];
@@ -186,9 +357,11 @@ __global__ __launch_bounds__(kGroupThreads) void df11_decode_kernel(DecodeArgs a
     __syncthreads();
 
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const int lane = (int)(threadIdx.x % kWave);
+    const uint32_t lane = threadIdx.x % kWave;
     uint8_t *tile = tiles + wave * kTileBytes;
     const uint32_t tile_addr = lds_offset(tile);
+    const uint8_t *lds_count = reinterpret_cast<const uint8_t *>(count_t);
+    const uint8_t *lds_dec = reinterpret_cast<const uint8_t *>(dec_t);
 
     // XCD-contiguous assignment: group g runs on XCD g % 8 and takes the
     // blocks of that XCD's range with a stride of (groups per XCD * waves)
@@ -199,148 +372,147 @@ __global__ __launch_bounds__(kGroupThreads) void df11_decode_kernel(DecodeArgs a
     uint32_t range_hi = range_lo + a.blocks_per_xcd;
     range_hi = range_hi < a.n_blocks ? range_hi : a.n_blocks;
     const uint32_t stride = groups_per_xcd * kWavesPerGroup;
+    const uint32_t first = range_lo + slot * kWavesPerGroup + wave;
 
-    const uint8_t *lds_count = reinterpret_cast<const uint8_t *>(count_t);
-    const uint8_t *lds_dec = reinterpret_cast<const uint8_t *>(dec_t);
+    // slice g = 64 b + lane: its stream dwords are 2g..2g+2 and its 5-bit
+    // gap field sits at bit 5 * lane of the block's 320 gap bits (dword 10 b)
+    auto stream_at = [&](uint32_t blk) { return a.stream + 2 * (blk * DF11_BLOCK_SLICES + lane); };
+    auto gaps_at = [&](uint32_t blk) { return a.gaps + 10 * blk + ((5 * lane) >> 5); };
+    const uint32_t gap_shift = (5 * lane) & 31;
 
-    for (uint32_t b = range_lo + slot * kWavesPerGroup + wave; b < range_hi; b += stride) {
-        const uint64_t g = (uint64_t)b * DF11_BLOCK_SLICES + (uint32_t)lane;
-        const uint32_t p0 = a.block_pos[b], p1 = a.block_pos[b + 1];
+    // block output positions of the wave's next 64 blocks: lane k holds block k's
+    uint32_t bp_lo = 0, bp_hi = 0;
+    uint32_t nd0 = 0, nd1 = 0, nd2 = 0, ng0 = 0, ng1 = 0;
+    if (first < range_hi) {
+        const uint32_t *sp = stream_at(first);
+        nd0 = sp[0], nd1 = sp[1], nd2 = sp[2];
+        const uint32_t *gp = gaps_at(first);
+        ng0 = gp[0], ng1 = gp[1];
+    }
+    // waited before the loop so that the loop header needs no wait (a wait
+    // there would also cover the previous block's stores)
+    asm volatile("" ::"v"(nd0), "v"(nd1), "v"(nd2), "v"(ng0), "v"(ng1));
+    uint32_t k = 0;
+    for (uint32_t b = first; b < range_hi; b += stride, ++k) {
+        if ((k & 63) == 0) {
+            const uint32_t mine = b + lane * stride;
+            bp_lo = mine < range_hi ? a.block_pos[mine] : 0u;
+            bp_hi = mine < range_hi ? a.block_pos[mine + 1] : 0u;
+            asm volatile("" ::"v"(bp_lo), "v"(bp_hi));  // waited here, not behind stores
+        }
+        const uint32_t p0 = __builtin_amdgcn_readlane(bp_lo, k & 63);
+        const uint32_t p1 = __builtin_amdgcn_readlane(bp_hi, k & 63);
+        const uint32_t d0 = nd0, d1 = nd1, d2 = nd2, gw0 = ng0, gw1 = ng1;
+        if (b + stride < range_hi) {  // the next block's inputs, consumed next iteration
+            const uint32_t *sp = stream_at(b + stride);
+            nd0 = sp[0], nd1 = sp[1], nd2 = sp[2];
+            const uint32_t *gp = gaps_at(b + stride);
+            ng0 = gp[0], ng1 = gp[1];
+        }
         const bool sane = p1 >= p0 && p1 <= a.n && p1 - p0 <= (uint32_t)kMaxBlockCodes;
-
-        // sign|mantissa for this lane's first output groups, loaded up front
         const uint32_t base = p0 & ~7u;
         const uint32_t groups = sane ? (p1 - base + 7) >> 3 : 0u;
+        const bool one_pass = groups * 8 + 4 <= (uint32_t)kTileCap;
+        // groups [full_lo, full_hi) lie inside [p0, p1) and get 16-byte stores;
+        // the partial head group (p0 unaligned) and tail group (p1 unaligned)
+        // are stored one element per lane: lanes 0-7 the head, 8-15 the tail
+        const uint32_t full_lo = p0 != base ? 1u : 0u;
+        const uint32_t full_hi = sane ? (p1 - base) >> 3 : 0u;
+        const uint32_t head_end = p0 != base ? (p1 < base + 8 ? p1 : base + 8) : p0;
+        const uint32_t tail_lo = base + 8 * full_hi > head_end ? base + 8 * full_hi : head_end;
+        const uint32_t edge_i = lane < 8 ? base + lane : base + 8 * full_hi + (lane - 8);
+        const bool edge = sane && lane < 16 &&
+                          (lane < 8 ? (edge_i >= p0 && edge_i < head_end)
+                                    : (edge_i >= tail_lo && edge_i < p1));
+        const uint32_t edge_sm = edge ? a.signmant[edge_i] : 0u;
+
+        // sign|mantissa of this lane's first output groups, loaded up front
         uint2 smv[kPrefetchGroups];
 #pragma unroll
         for (int i = 0; i < kPrefetchGroups; ++i) {
-            const uint32_t j = (uint32_t)lane + kWave * i;
-            smv[i] = j < groups ? *reinterpret_cast<const uint2 *>(a.signmant + base + 8 * j)
-                                : make_uint2(0, 0);
+            const uint32_t j = lane + kWave * i;
+            smv[i] = one_pass && j < groups
+                         ? *reinterpret_cast<const uint2 *>(a.signmant + base + 8 * j)
+                         : make_uint2(0, 0);
         }
 
-        const uint32_t *sp = a.stream + 2 * g;
-        const uint32_t d0 = sp[0], d1 = sp[1], d2 = sp[2];
-        const uint64_t q = 5 * g;  // bit offset of this slice's gap field
-        const uint32_t *gp = a.gaps + (q >> 5);
-        const uint32_t gw = __builtin_amdgcn_alignbit(gp[1], gp[0], (uint32_t)(q & 31));
-        const int gap = (int)(gw & 31u), gap_next = (int)((gw >> 5) & 31u);
-        const int64_t rel = (int64_t)a.stop_bit - (int64_t)(g * DF11_SLICE_BITS);
-        const int lim = rel <= 0 ? 0 : (rel >= 64 ? 64 : (int)rel);
-        // end of this lane's last code: the next slice's first code start, or
-        // the end of the stream for the lane holding the final code
-        const int end = rel > 0 && rel <= 64
-                            ? (int)((int64_t)a.total_bits - (int64_t)(g * DF11_SLICE_BITS))
-                            : 64 + gap_next;
+        const uint32_t gw = __builtin_amdgcn_alignbit(gw1, gw0, gap_shift);
+        const uint32_t gap = gw & 31u, gap_next = (gw >> 5) & 31u;
+        const uint64_t g64 = (uint64_t)b * DF11_BLOCK_SLICES + lane;
+        const int64_t rel = (int64_t)a.stop_bit - (int64_t)(g64 * DF11_SLICE_BITS);
+        // codes of this lane start in [gap, lim); the last one ends at `end`:
+        // the next slice's first code start, or the stream's end for the lane
+        // holding the final code
+        const uint32_t lim = rel <= 0 ? 0u : (rel >= 64 ? 64u : (uint32_t)rel);
+        const uint32_t end = rel > 0 && rel <= 64
+                                 ? (uint32_t)((int64_t)a.total_bits - (int64_t)(g64 * DF11_SLICE_BITS))
+                                 : 64u + gap_next;
 
         // ---- phase 1: count
-        uint32_t cnt;
-        {
-            const uint32_t f0 = pad_ones(d0, end, 0), f1 = pad_ones(d1, end, 32),
-                           f2 = pad_ones(d2, end, 64);
-            // pre-shift by 2: window bits [2, 2+W) are the entry's byte offset / 4 * 4
-            const uint32_t c0 = f0 << 2, c1 = __builtin_amdgcn_alignbit(f1, f0, 30),
-                           c2 = __builtin_amdgcn_alignbit(f2, f1, 30);
-            constexpr uint32_t kMask = ((1u << kCountBits) - 1) << 2;
-            uint32_t acc = lim > 0 ? (uint32_t)gap : 0u;  // pos | count << 16
-            const uint32_t stop1 = lim > 0 ? (uint32_t)end : 0u;
-            const uint32_t stop0 = stop1 < 32u ? stop1 : 32u;
-            while ((acc & 0xFFFFu) < stop0) {
-                const uint32_t w = __builtin_amdgcn_alignbit(c1, c0, acc);
-                uint32_t x = *reinterpret_cast<const uint32_t *>(lds_count + (w & kMask));
-                if (x < 0x10000u) {
-                    const uint32_t e = lookup8(lut, __builtin_amdgcn_alignbit(d1, d0, acc), a.n_tables);
-                    x = leaf_len(e) | 0x10000u;
-                }
-                acc += x;
-            }
-            while ((acc & 0xFFFFu) < stop1) {
-                const uint32_t w = __builtin_amdgcn_alignbit(c2, c1, acc);
-                uint32_t x = *reinterpret_cast<const uint32_t *>(lds_count + (w & kMask));
-                if (x < 0x10000u) {
-                    const uint32_t e = lookup8(lut, __builtin_amdgcn_alignbit(d2, d1, acc), a.n_tables);
-                    x = leaf_len(e) | 0x10000u;
-                }
-                acc += x;
-            }
-            cnt = acc >> 16;
-        }
+        const uint32_t cnt =
+            lim ? count_codes(lds_count, lut, a.n_tables, d0, d1, d2, pad_ones(d0, (int)end, 0),
+                              pad_ones(d1, (int)end, 32), pad_ones(d2, (int)end, 64), gap, end)
+                : 0u;
 
-        // wave-wide inclusive scan of the counts
-        uint32_t incl = cnt;
-#pragma unroll
-        for (int off = 1; off < kWave; off <<= 1) {
-            const uint32_t y = __shfl_up(incl, off, kWave);
-            if (lane >= off) incl += y;
-        }
+        // wave-wide prefix sum of the counts
+        const uint32_t incl = wave_inclusive_sum(cnt);
         const uint32_t excl = incl - cnt;
-        const uint32_t total = __shfl(incl, kWave - 1, kWave);
-        if ((!sane || total != p1 - p0) && lane == 0 && a.status) atomicAdd(a.status, 1u);
-        if (!sane) continue;
-
-        // ---- phase 2: decode into the tile
-        {
-            const uint32_t r0 = d0 << 3, r1 = __builtin_amdgcn_alignbit(d1, d0, 29),
-                           r2 = __builtin_amdgcn_alignbit(d2, d1, 29);
-            constexpr uint32_t kMask = ((1u << kDecodeBits) - 1) << 3;
-            // pos | (LDS address of the next exponent byte) << 16
-            uint32_t acc = (lim > 0 ? (uint32_t)gap : 0u) |
-                           ((tile_addr + (p0 - base) + excl) << 16);
-            const uint32_t stop1 = (uint32_t)lim;
-            const uint32_t stop0 = stop1 < 32u ? stop1 : 32u;
-#define DF11_DECODE_STEP(HI, LO, DHI, DLO)                                                      \
-    {                                                                                            \
-        const uint32_t w = __builtin_amdgcn_alignbit(HI, LO, acc);                               \
-        const uint2 dv = *reinterpret_cast<const uint2 *>(lds_dec + (w & kMask));                \
-        lds_u8 *o = (lds_u8 *)(uintptr_t)(acc >> 16);                                            \
-        if (dv.x < 0x1000000u) {                                                                 \
-            const uint32_t e = lookup8(lut, __builtin_amdgcn_alignbit(DHI, DLO, acc), a.n_tables);\
-            o[0] = (uint8_t)e;                                                                   \
-            acc += leaf_len(e) | 0x10000u;                                                       \
-        } else {                                                                                 \
-            o[0] = (uint8_t)dv.x;                                                                \
-            if (dv.x >= 0x2000000u) o[1] = (uint8_t)(dv.x >> 16);                                \
-            if (dv.x >= 0x3000000u) o[2] = (uint8_t)dv.y;                                        \
-            if (dv.x >= 0x4000000u) o[3] = (uint8_t)(dv.y >> 16);                                \
-            acc += __builtin_amdgcn_perm(dv.x, dv.x, 0x0C030C01u);                               \
-        }                                                                                        \
-    }
-            while ((acc & 0xFFFFu) < stop0) DF11_DECODE_STEP(r1, r0, d1, d0)
-            while ((acc & 0xFFFFu) < stop1) DF11_DECODE_STEP(r2, r1, d2, d1)
-#undef DF11_DECODE_STEP
+        const uint32_t total = __builtin_amdgcn_readlane(incl, kWave - 1);
+        // vmcnt is an in-order counter that also counts stores: take the wait
+        // for the next block's prefetched inputs here, on every path and before
+        // this block's stores are issued, so that no later wait (the loop
+        // header's in particular) has to cover those stores
+        asm volatile("" ::"v"(nd0), "v"(nd1), "v"(nd2), "v"(ng0), "v"(ng1));
+        // a count that disagrees with block_pos means a corrupt block: report
+        // it and leave its output unwritten
+        if (!sane || total != p1 - p0) {
+            if (lane == 0 && a.status) atomicAdd(a.status, 1u);
+            continue;
         }
-        wave_lds_sync();
+        const uint32_t at = (p0 - base) + excl;  // tile position of this lane's first symbol
+        const uint32_t stop = lim ? lim : 0u;
+        const uint32_t start = lim ? gap : 0u;
 
-        // ---- merge with sign|mantissa, 8 BF16 per lane per 16-byte store
+        if (one_pass) {
+            // ---- phase 2: decode into the tile, then restore each lane's head
+            decode_codes<false>(lds_dec, lut, a.n_tables, d0, d1, d2, start, stop, tile_addr, at, 0);
+            wave_lds_sync();
+            rewrite_head(lds_dec, lut, a.n_tables, d0, d1, d2, start, cnt, tile_addr + at);
+            wave_lds_sync();
+            // ---- merge with sign|mantissa, 8 BF16 per lane per 16-byte store
 #pragma unroll
-        for (int i = 0; i < kPrefetchGroups; ++i) {
-            const uint32_t j = (uint32_t)lane + kWave * i;
-            if (j < groups) {
-                const uint32_t i0 = base + 8 * j;
-                const uint4 o = join8(*reinterpret_cast<const uint2 *>(tile + 8 * j), smv[i]);
-                if (i0 >= p0 && i0 + 8 <= p1) {
-                    *reinterpret_cast<uint4 *>(a.out + i0) = o;
-                } else {
-                    const uint32_t ow[4] = {o.x, o.y, o.z, o.w};
-                    for (uint32_t k = 0; k < 8; ++k)
-                        if (i0 + k >= p0 && i0 + k < p1)
-                            a.out[i0 + k] = (uint16_t)(ow[k >> 1] >> (16 * (k & 1)));
+            for (int i = 0; i < kPrefetchGroups; ++i) {
+                const uint32_t j = lane + kWave * i;
+                if (j >= full_lo && j < full_hi)
+                    *reinterpret_cast<uint4 *>(a.out + base + 8 * j) =
+                        join8(*reinterpret_cast<const uint2 *>(tile + 8 * j), smv[i]);
+            }
+            for (uint32_t j = lane + kWave * kPrefetchGroups; j < full_hi; j += kWave) {
+                const uint2 sm = *reinterpret_cast<const uint2 *>(a.signmant + base + 8 * j);
+                *reinterpret_cast<uint4 *>(a.out + base + 8 * j) =
+                    join8(*reinterpret_cast<const uint2 *>(tile + 8 * j), sm);
+            }
+            if (edge) a.out[edge_i] = (uint16_t)join1(tile[edge_i - base], edge_sm);
+            wave_lds_sync();
+        } else {
+            // more symbols than one tile holds: decode again per tile-sized window
+            for (uint32_t r0 = 0; r0 < groups * 8; r0 += kTileCap) {
+                decode_codes<true>(lds_dec, lut, a.n_tables, d0, d1, d2, start, stop, tile_addr,
+                                   at, r0);
+                wave_lds_sync();
+                const uint32_t j_hi = (r0 + kTileCap) / 8 < groups ? (r0 + kTileCap) / 8 : groups;
+                for (uint32_t j = r0 / 8 + lane; j < j_hi; j += kWave) {
+                    if (j < full_lo || j >= full_hi) continue;  // edge groups: below
+                    const uint2 sm = *reinterpret_cast<const uint2 *>(a.signmant + base + 8 * j);
+                    *reinterpret_cast<uint4 *>(a.out + base + 8 * j) =
+                        join8(*reinterpret_cast<const uint2 *>(tile + 8 * j - r0), sm);
                 }
+                const uint32_t er = edge_i - base - r0;
+                if (edge && er < (uint32_t)kTileCap)
+                    a.out[edge_i] = (uint16_t)join1(tile[er], edge_sm);
+                wave_lds_sync();
             }
         }
-        for (uint32_t j = (uint32_t)lane + kWave * kPrefetchGroups; j < groups; j += kWave) {
-            const uint32_t i0 = base + 8 * j;
-            const uint2 s = *reinterpret_cast<const uint2 *>(a.signmant + i0);
-            const uint4 o = join8(*reinterpret_cast<const uint2 *>(tile + 8 * j), s);
-            if (i0 + 8 <= p1) {
-                *reinterpret_cast<uint4 *>(a.out + i0) = o;
-            } else {
-                const uint32_t ow[4] = {o.x, o.y, o.z, o.w};
-                for (uint32_t k = 0; k < 8; ++k)
-                    if (i0 + k < p1) a.out[i0 + k] = (uint16_t)(ow[k >> 1] >> (16 * (k & 1)));
-            }
-        }
-        wave_lds_sync();
     }
 }
 
@@ -350,10 +522,8 @@ constexpr int kMaxDevices = 16;
 std::atomic<int> g_cus[kMaxDevices];
 std::atomic<int> g_occ[kMaxDevices][DF11_MAX_TABLES + 1];
 
-// dynamic LDS per workgroup (the two multi-code tables are static)
-size_t lds_bytes(uint32_t n_tables) {
-    return (size_t)n_tables * kTableBytes + (size_t)kWavesPerGroup * kTileBytes;
-}
+// dynamic LDS per workgroup: the 8-bit tables (tiles and fast tables are static)
+size_t lds_bytes(uint32_t n_tables) { return (size_t)n_tables * kTableBytes; }
 
 int launch_groups(int dev, uint32_t n_tables, uint32_t n_blocks, int *groups) {
     if (dev < 0 || dev >= kMaxDevices) return DF11_ERR_HIP;
@@ -365,10 +535,20 @@ int launch_groups(int dev, uint32_t n_tables, uint32_t n_blocks, int *groups) {
     }
     int occ = g_occ[dev][n_tables].load(std::memory_order_relaxed);
     if (occ <= 0) {
+        // a workgroup whose LDS exceeds what one CU can give it would never be
+        // dispatched: refuse the launch instead
+        int max_lds = 0;
+        hipFuncAttributes attr;
+        if (hipDeviceGetAttribute(&max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) !=
+                hipSuccess ||
+            hipFuncGetAttributes(&attr, reinterpret_cast<const void *>(df11_decode_kernel)) !=
+                hipSuccess)
+            return DF11_ERR_HIP;
+        if (attr.sharedSizeBytes + lds_bytes(n_tables) > (size_t)max_lds) return DF11_ERR_TABLES;
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, df11_decode_kernel, kGroupThreads,
                                                          lds_bytes(n_tables)) != hipSuccess)
             return DF11_ERR_HIP;
-        if (occ <= 0) occ = 1;
+        if (occ <= 0) return DF11_ERR_TABLES;
         g_occ[dev][n_tables].store(occ, std::memory_order_relaxed);
     }
     // a multiple of the XCD count, no more than there are blocks to share
