@@ -85,6 +85,64 @@ def cpu_baseline(wlx, enc) -> dict:
                       f"of every code from bit 0, then BF16 join, 1 thread"}
 
 
+def run_copy(args) -> int:
+    """A plain device-to-device copy of known size: the reference that the HBM
+    byte counters of a profiler run are scaled by."""
+    import torch
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    nbytes = args.copy_mib << 20
+    src = torch.empty(nbytes // 2, dtype=torch.int16, device=dev).random_(-100, 100)
+    dst = torch.empty_like(src)
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(args.warmup):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    for k in range(args.steps):
+        starts[k].record(stream)
+        dst.copy_(src)
+        ends[k].record(stream)
+    torch.cuda.synchronize()
+    ms = sum(s.elapsed_time(e) for s, e in zip(starts, ends)) / args.steps
+    print(json.dumps({"mode": "copy", "bytes_read": nbytes, "bytes_written": nbytes,
+                      "kernel_ms": round(ms, 5),
+                      "GBps_read_plus_write": round(2 * nbytes / (ms * 1e-3) / 1e9, 1),
+                      "ok": bool(torch.equal(src, dst))}), flush=True)
+    return 0
+
+
+def gemm_ratios(wlx, out, decode_ms, stream, batches=(1, 64), reps=10) -> dict:
+    """Decode time of the block over the time of the block's bf16 GEMMs
+    (y = x W^T for each of its matrices, on the decoded weights) at each batch."""
+    import torch
+    res = {}
+    mats, off = [], 0
+    for m in wlx.matrices:
+        mats.append(out[off: off + m.rows * m.cols].view(m.rows, m.cols))
+        off += m.rows * m.cols
+    g = torch.Generator(device=out.device).manual_seed(7)
+    for b in batches:
+        xs = [torch.randn(b, w.shape[1], device=out.device, generator=g).to(torch.bfloat16)
+              for w in mats]
+        for _ in range(2):
+            for x, w in zip(xs, mats):
+                torch.nn.functional.linear(x, w)
+        torch.cuda.synchronize()
+        s0 = torch.cuda.Event(enable_timing=True)
+        s1 = torch.cuda.Event(enable_timing=True)
+        s0.record(stream)
+        for _ in range(reps):
+            for x, w in zip(xs, mats):
+                torch.nn.functional.linear(x, w)
+        s1.record(stream)
+        torch.cuda.synchronize()
+        gms = s0.elapsed_time(s1) / reps
+        res[f"batch{b}"] = {"gemm_ms": round(gms, 5), "decode_over_gemm": round(decode_ms / gms, 4)}
+    return res
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -94,12 +152,20 @@ def main() -> int:
     ap.add_argument("--copies", type=int, default=3,
                     help="rotating encoded copies (defeats the Infinity Cache)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-gemm", action="store_true", help="skip the decode/GEMM ratios")
+    ap.add_argument("--mode", choices=("decode", "copy"), default="decode",
+                    help="copy: time a plain device copy of --copy-mib MiB instead")
+    ap.add_argument("--copy-mib", type=int, default=1024)
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; the decode shards "
-                                   "without communication (see DESIGN.md), but --gpus must be 1"}))
+        print(json.dumps({"error": "df11_decode is measured on one GPU only (--gpus 1); "
+                                   "across GPUs the decode shards by whole blocks with no "
+                                   "communication, so no multi-GPU figure is produced"}))
         return 2
+
+    if args.mode == "copy":
+        return run_copy(args)
 
     import numpy as np
     import torch
@@ -174,6 +240,8 @@ def main() -> int:
                      "traffic": traffic,
                      "bytes_per_launch": {"read": rd, "written": wr}},
     }
+    if not args.no_gemm:
+        line["decode_vs_gemm"] = gemm_ratios(wlx, out, avg_ms, stream)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wlx, enc)
     print(json.dumps(line), flush=True)

@@ -28,6 +28,10 @@
  * Readings where the page is silent (each is listed in the design notes):
  *   - Length limit: while the longest code exceeds the limit, every nonzero
  *     count c becomes (c + 1) / 2 (integer division) and the tree is rebuilt.
+ *     Parity unpinned for the exact lengths when the limit binds: the page
+ *     fixes no rule, so only invariants pin them (longest code within the
+ *     limit, Kraft equality, cost between the unlimited and the brute-force
+ *     limited optimum, plain Huffman when the limit does not bind).
  *   - Packed bit order: stream bit k is bit (k mod 8) of byte k / 8 (least
  *     significant bit first inside a byte; the page keeps an unpacked array).
  *   - A slice is 64 bits; a block is 64 slices (4096 bits, 512 bytes).
