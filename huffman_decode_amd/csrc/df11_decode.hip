@@ -14,24 +14,27 @@
 //  * a format block (64 slices, 512 stream bytes) is one wave64, so the prefix
 //    sum is a wave-level scan and no workgroup barrier sits in the block loop;
 //  * workgroups are persistent; each stages the 8-bit tables and expands them
-//    in LDS into two multi-code tables indexed by the next W stream bits:
-//      count table  : bits taken by all codes that end inside the W bits, and
-//                     their number (phase 1 counts ~4 codes per lookup);
-//      decode table : the first (up to 4) of those symbols, bits and count
-//                     (phase 2 stores up to 4 exponents per lookup with one
-//                     4-byte LDS store; ROCm runs gfx9 LDS in unaligned mode);
-//    codes longer than W fall back to the 8-bit tables;
+//    in LDS into a multi-code decode table indexed by the next 11 stream bits:
+//    each entry holds the first (up to 4) codes that end inside a window
+//    narrower than the longest code -- their symbols packed in one dword,
+//    their total length and their number -- so one lookup yields up to 4
+//    exponents, stored with one 4-byte LDS store (ROCm runs gfx9 LDS in
+//    unaligned mode); codes longer than the window fall back to the 8-bit
+//    tables;
 //  * a lane's 96 relevant stream bits live in three VGPRs; windows come from
 //    one funnel shift (v_alignbit) of a dword pair, with the data pre-shifted
 //    so that the window's low bits are already the table's byte offset;
-//  * bits after the lane's last code are forced to 1 for phase 1: the all-ones
-//    prefix is the longest code's prefix, which never completes inside the
-//    count window (its width is kept below the longest code), so a lookup
-//    never counts the next lane's codes; phase 2 reads the real bits, so any
-//    symbol it decodes past the lane's end is the true next symbol;
-//  * phase 2 writes exponent bytes into a per-wave LDS tile aligned to 8
-//    outputs; the merge joins 8 exponents with 8 prefetched sign|mantissa
-//    bytes per lane and writes one 16-byte store;
+//  * the phases are merged: phase 1 decodes each lane's codes once, into a
+//    private 40-byte staging slot in LDS, and its step count is the lane's
+//    code count.  The count is exact because the bits after the lane's last
+//    code are forced to 1 for these lookups: all ones is a prefix of the
+//    longest code, which never completes inside the window.  After the scan
+//    each lane copies its staged exponents to its output position in the
+//    wave's tile.  Lanes with more codes than a slot holds (only near-flat
+//    streams of 1- and 2-bit codes) send their wave down the page's own
+//    route: decode the real bits again, straight into the tile;
+//  * the merge joins 8 exponents with 8 prefetched sign|mantissa bytes per
+//    lane and writes one 16-byte store;
 //  * blocks are split into 8 contiguous ranges, one per XCD (workgroups are
 //    dispatched round-robin over the XCDs), so neighbouring blocks, which
 //    share cache lines at their edges, meet in the same L2.
@@ -48,9 +51,6 @@ namespace {
 #ifndef DF11_WAVES_PER_GROUP
 #define DF11_WAVES_PER_GROUP 8
 #endif
-#ifndef DF11_COUNT_BITS
-#define DF11_COUNT_BITS 11
-#endif
 #ifndef DF11_DECODE_BITS
 #define DF11_DECODE_BITS 11
 #endif
@@ -58,30 +58,42 @@ namespace {
 constexpr int kWave = 64;
 constexpr int kWavesPerGroup = DF11_WAVES_PER_GROUP;
 constexpr int kGroupThreads = kWave * kWavesPerGroup;
-#ifndef DF11_TILE_SYMBOLS
-#define DF11_TILE_SYMBOLS 2048
-#endif
 constexpr int kMaxBlockCodes = DF11_BLOCK_SLICES * DF11_SLICE_BITS;  // all 1-bit codes
-// exponent bytes one tile holds; blocks with more symbols take several passes
-constexpr int kTileCap = DF11_TILE_SYMBOLS;
-constexpr int kTileBytes = kTileCap + 16;
+// staging: lane t's phase-1 exponents at byte 4 + 40 t of its wave's LDS
+// region (the 4 bytes in front let every lane read the dword before its slot);
+// a lane with more than 32 codes, or with fewer than 3 before the block's last
+// code, sends the wave to the re-decode route
+constexpr int kStageBase = 4;
+constexpr int kStageStride = 40;
+constexpr int kStageCodes = 32;
+constexpr int kStageMinCodes = 3;
+// exponent bytes one tile holds (the tile reuses the wave's staging region);
+// blocks with more symbols take several passes
+constexpr int kTileCap = 2560;
+// a lane's stores reach at most 3 bytes past its last code; a lane holds at
+// most 64 codes, so 4 + 63 * 40 + 67 bytes bound the staging stores of valid data
+constexpr int kTileBytes = kTileCap + 32;
 static_assert(kTileCap % 8 == 0, "tile windows must stay 8-aligned");
+static_assert(kTileBytes >= kStageBase + 63 * kStageStride + 64 + 3, "staging must fit");
+static_assert(kStageStride % 4 == 0 && kStageBase % 4 == 0 && kTileBytes % 8 == 0,
+              "staging dwords are aligned");
+static_assert(kStageStride >= kStageCodes + 4, "a full slot takes 4 stray bytes");
 constexpr int kTableBytes = 256 * 2;
 constexpr int kXcds = 8;
 
-// multi-code tables (LDS): window widths
-constexpr int kCountBits = DF11_COUNT_BITS;
+// multi-code decode table (LDS): index width
 constexpr int kDecodeBits = DF11_DECODE_BITS;
-constexpr int kCountBytes = (1 << kCountBits) * 4;
 constexpr int kDecodeBytes = (1 << kDecodeBits) * 8;
 constexpr int kMaxSymbolsPerStep = 4;
 constexpr int kTilesBytes = kWavesPerGroup * kTileBytes;
-constexpr int kStaticLds = kTilesBytes + kCountBytes + kDecodeBytes;
+constexpr int kStaticLds = kTilesBytes + kDecodeBytes;
 static_assert(kTilesBytes < 0x10000, "tile addresses must fit 16 bits");
 constexpr int kPrefetchGroups = 4;  // sign|mantissa groups of 8 per lane loaded up front
 
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
+typedef __attribute__((address_space(3))) uint16_t lds_u16;
 typedef __attribute__((address_space(3))) uint32_t lds_u32;
+typedef __attribute__((address_space(3))) uint64_t lds_u64;
 
 __device__ __forceinline__ uint32_t lds_offset(const void *p) {
     // low 32 bits of a flat address inside the LDS aperture are the LDS offset
@@ -121,36 +133,25 @@ __device__ __forceinline__ uint32_t lookup8(const uint16_t *lut, uint32_t w, uin
 
 __device__ __forceinline__ uint32_t leaf_len(uint32_t e) { return ((e >> 8) & 31u) + 1u; }
 
-// Expand the 8-bit tables into the count and decode tables (whole workgroup).
-__device__ void build_fast_tables(const uint16_t *lut, uint32_t *count_t, uint2 *dec_t,
-                                  uint32_t n_tables, uint32_t max_len) {
-    // the count window must stay shorter than the longest code (see header)
-    const uint32_t count_w = max_len - 1 < (uint32_t)kCountBits ? max_len - 1 : kCountBits;
-    constexpr int kEntries = (1 << kCountBits) > (1 << kDecodeBits) ? (1 << kCountBits)
-                                                                     : (1 << kDecodeBits);
-    constexpr uint32_t kSpan = kCountBits > kDecodeBits ? kCountBits : kDecodeBits;
-    for (int i = threadIdx.x; i < kEntries; i += kGroupThreads) {
-        // codes of the bit pattern i (first stream bit in bit 0; zeros past
-        // the table width never complete a code that is counted)
-        uint32_t pos = 0, k = 0, cpos = 0, ck = 0, dpos = 0, dk = 0;
-        uint32_t s0123 = 0;
-        for (uint32_t step = 0; step < kSpan; ++step) {
+// Expand the 8-bit tables into the decode table (whole workgroup).  An entry
+// covers the codes that end within the first `width` bits of its index, at
+// most four: their length in bits | their number << 16, then the symbols one
+// per byte (unused bytes 0).  width = min(longest code - 1, 11): all ones is a
+// prefix of the longest code, so a run of ones never completes a code here.
+__device__ void build_decode_table(const uint16_t *lut, uint2 *dec_t, uint32_t n_tables,
+                                   uint32_t max_len) {
+    const uint32_t width = max_len - 1 < (uint32_t)kDecodeBits ? max_len - 1 : kDecodeBits;
+    for (int i = threadIdx.x; i < (1 << kDecodeBits); i += kGroupThreads) {
+        uint32_t pos = 0, k = 0, syms = 0;
+        while (k < (uint32_t)kMaxSymbolsPerStep) {
             const uint32_t e = lookup8(lut, (uint32_t)i >> pos, n_tables);
             const uint32_t len = leaf_len(e);
-            if (pos + len > kSpan) break;
-            if (pos + len <= count_w) cpos = pos + len, ck = k + 1;
-            if (pos + len <= (uint32_t)kDecodeBits && k < (uint32_t)kMaxSymbolsPerStep) {
-                s0123 |= (e & 0xFFu) << (8 * k);
-                dpos = pos + len;
-                dk = k + 1;
-            }
+            if (pos + len > width) break;
+            syms |= (e & 0xFFu) << (8 * k);
             pos += len;
             ++k;
         }
-        if (i < (1 << kCountBits)) count_t[i] = cpos | (ck << 16);
-        // decode entry: bits | count << 16 (added to the accumulator as is),
-        // then the symbols packed one per byte
-        if (i < (1 << kDecodeBits)) dec_t[i] = make_uint2(dpos | (dk << 16), s0123);
+        dec_t[i] = make_uint2(pos | (k << 16), syms);
     }
 }
 
@@ -199,35 +200,79 @@ __device__ __forceinline__ uint32_t pad_ones(uint32_t d, int end, int base) {
     return d | (0xFFFFFFFFu << keep);
 }
 
-// Phase 1 for one lane: number of codes starting in [pos, stop) of its slice.
-// f* are the slice's dwords with the bits after its last code set to 1,
-// d* the plain dwords (for codes longer than the count window).
-__device__ __forceinline__ uint32_t count_codes(const uint8_t *lds_count, const uint16_t *lut,
+// Phase 1 for one lane: decode the codes starting in [pos, stop) of its slice
+// into its staging slot at LDS address `slot`, four bytes per table step, and
+// return their number.  f* are the slice's dwords with the bits after its last
+// code set to 1 (so a step never runs past that code and the count is exact),
+// d* the plain dwords (for codes longer than the table window).  Stores are
+// clamped to `clamp` so that corrupt input cannot reach past the wave's
+// region; valid data never gets there.
+__device__ __forceinline__ uint32_t stage_codes(const uint8_t *lds_dec, const uint16_t *lut,
                                                 uint32_t n_tables, uint32_t d0, uint32_t d1,
                                                 uint32_t d2, uint32_t f0, uint32_t f1, uint32_t f2,
-                                                uint32_t pos, uint32_t stop) {
-    // pre-shift by 2: window bits [2, 2+W) are the entry's byte offset
-    const uint32_t c0 = f0 << 2, c1 = __builtin_amdgcn_alignbit(f1, f0, 30),
-                   c2 = __builtin_amdgcn_alignbit(f2, f1, 30);
-    constexpr uint32_t kMask = ((1u << kCountBits) - 1) << 2;
-    uint32_t acc = pos;  // pos | count << 16
+                                                uint32_t pos, uint32_t stop, uint32_t slot,
+                                                uint32_t clamp) {
+    // pre-shift by 3: window bits [3, 3+W) are the entry's byte offset
+    const uint32_t e0 = f0 << 3, e1 = __builtin_amdgcn_alignbit(f1, f0, 29),
+                   e2 = __builtin_amdgcn_alignbit(f2, f1, 29);
+    constexpr uint32_t kMask = ((1u << kDecodeBits) - 1) << 3;
+    uint32_t acc = pos | (slot << 16);  // pos | (LDS address of the next byte) << 16
+    auto step = [&](uint32_t hi, uint32_t lo, uint32_t dhi, uint32_t dlo) {
+        const uint32_t w = __builtin_amdgcn_alignbit(hi, lo, acc);
+        const uint2 dv = *reinterpret_cast<const uint2 *>(lds_dec + (w & kMask));
+        uint32_t at = acc >> 16;
+        at = at < clamp ? at : clamp;
+        *(lds_u32 *)(uintptr_t)at = dv.y;
+        uint32_t inc = dv.x;
+        if (dv.x < 0x10000u) {  // longer than the window: 8-bit tables, real bits
+            const uint32_t e = lookup8(lut, __builtin_amdgcn_alignbit(dhi, dlo, acc), n_tables);
+            *(lds_u8 *)(uintptr_t)at = (uint8_t)e;
+            inc = leaf_len(e) | 0x10000u;
+        }
+        acc += inc;
+    };
     const uint32_t stop0 = stop < 32u ? stop : 32u;
     // a half holds at most 32 code starts: the bound only matters for corrupt input
-    for (int it = 0; it < 32 && (acc & 0xFFFFu) < stop0; ++it) {
-        const uint32_t w = __builtin_amdgcn_alignbit(c1, c0, acc);
-        uint32_t x = *reinterpret_cast<const uint32_t *>(lds_count + (w & kMask));
-        if (x < 0x10000u)
-            x = leaf_len(lookup8(lut, __builtin_amdgcn_alignbit(d1, d0, acc), n_tables)) | 0x10000u;
-        acc += x;
+    for (int it = 0; it < 32 && (acc & 0xFFFFu) < stop0; ++it) step(e1, e0, d1, d0);
+    for (int it = 0; it < 32 && (acc & 0xFFFFu) < stop; ++it) step(e2, e1, d2, d1);
+    return (acc >> 16) - slot;
+}
+
+// After the scan: move the lane's `cnt` staged exponents (at most 32) from its
+// slot to tile address `dst` with aligned dword stores only.  The lane writes
+// every aligned dword that ends inside its own output bytes; the first of
+// them starts with the previous lane's last bytes (`prev`, taken from that
+// lane's slot), and the lane holding the block's last code (`last_lane`) also
+// writes its final, partial dword.  Every tile dword is thus written exactly
+// once, provided each lane before the last one holds at least 3 codes.
+__device__ __forceinline__ void place_staged(uint32_t slot, uint32_t dst, uint32_t cnt,
+                                             uint32_t prev, bool last_lane) {
+    uint32_t v[9];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = *(const lds_u32 *)(uintptr_t)(slot + 4 * i);
+    v[8] = 0;
+    const uint32_t s = dst & 3u, a0 = dst & ~3u;
+    // byte t of output dword j is byte 4 j + t - s of the lane's sequence;
+    // v_perm picks it from {v[j], v[j - 1]} (bytes 4..7 and 0..3)
+    const uint32_t sel = 0x07060504u - s * 0x01010101u;
+    const int last = cnt == 0 ? -1
+                     : last_lane ? (int)((s + cnt - 1) >> 2)
+                                 : (int)((s + cnt) >> 2) - 1;
+#pragma unroll
+    for (int j = 0; j < 9; ++j) {
+        const uint32_t val = __builtin_amdgcn_perm(v[j], j ? v[j - 1] : prev, sel);
+        if (j <= last) *(lds_u32 *)(uintptr_t)(a0 + 4 * j) = val;
     }
-    for (int it = 0; it < 32 && (acc & 0xFFFFu) < stop; ++it) {
-        const uint32_t w = __builtin_amdgcn_alignbit(c2, c1, acc);
-        uint32_t x = *reinterpret_cast<const uint32_t *>(lds_count + (w & kMask));
-        if (x < 0x10000u)
-            x = leaf_len(lookup8(lut, __builtin_amdgcn_alignbit(d2, d1, acc), n_tables)) | 0x10000u;
-        acc += x;
-    }
-    return acc >> 16;
+}
+
+// The 4 bytes of a lane's slot that end at its last code (the first byte is
+// junk when it holds 3 codes).
+__device__ __forceinline__ uint32_t staged_tail(uint32_t slot, uint32_t cnt) {
+    const int b = (int)cnt - 4;  // >= -4: the slot is preceded by 4 bytes
+    const uint32_t at = (uint32_t)((int)slot + (b & ~3));
+    const uint32_t lo = *(const lds_u32 *)(uintptr_t)at;
+    const uint32_t hi = *(const lds_u32 *)(uintptr_t)(at + 4);
+    return __builtin_amdgcn_alignbit(hi, lo, 8u * (uint32_t)(b & 3));
 }
 
 // Phase 2 for one lane: decode the codes starting in [pos, stop) and store
@@ -332,15 +377,20 @@ __device__ __forceinline__ uint32_t join1(uint32_t e, uint32_t sm) {
     return ((sm & 0x80u) << 8) | ((e & 0xFFu) << 7) | (sm & 0x7Fu);
 }
 
-__global__ __launch_bounds__(kGroupThreads) void df11_decode_kernel(DecodeArgs a) {
-    // LDS: per-wave exponent tiles | count table | decode table in one static
-    // array (fixed offsets fold into the ds_read/ds_write immediates, and the
-    // tiles sit at the lowest addresses so a tile address fits the 16-bit field
-    // of the phase-2 accumulator), then the 8-bit tables in dynamic LDS.
+#ifdef DF11_WAVES_PER_EU
+#define DF11_OCCUPANCY_HINT __attribute__((amdgpu_waves_per_eu(DF11_WAVES_PER_EU)))
+#else
+#define DF11_OCCUPANCY_HINT
+#endif
+__global__ __launch_bounds__(kGroupThreads) DF11_OCCUPANCY_HINT void df11_decode_kernel(DecodeArgs a) {
+    // LDS: per-wave regions (staging slots, then the exponent tile) | decode
+    // table in one static array (fixed offsets fold into the ds_read/ds_write
+    // immediates, and the regions sit at the lowest addresses so that their
+    // addresses fit the 16-bit field of the phase accumulators), then the 8-bit
+    // tables in dynamic LDS.
     __shared__ __attribute__((aligned(16))) uint8_t lds_static[kStaticLds];
     uint8_t *tiles = lds_static;
-    uint32_t *count_t = reinterpret_cast<uint32_t *>(lds_static + kTilesBytes);
-    uint2 *dec_t = reinterpret_cast<uint2 *>(lds_static + kTilesBytes + kCountBytes);
+    uint2 *dec_t = reinterpret_cast<uint2 *>(lds_static + kTilesBytes);
     extern __shared__ uint4 smem_u4[];
     uint16_t *lut = reinterpret_cast<uint16_t *>(smem_u4);
     const uint32_t hier_bytes = a.n_tables * kTableBytes;
@@ -353,14 +403,13 @@ __global__ __launch_bounds__(kGroupThreads) void df11_decode_kernel(DecodeArgs a
     uint4 *lut_u4 = reinterpret_cast<uint4 *>(lut);
     for (uint32_t i = threadIdx.x; i < hier_bytes / 16; i += kGroupThreads) lut_u4[i] = a.luts[i];
     __syncthreads();
-    build_fast_tables(lut, count_t, dec_t, a.n_tables, a.max_len);
+    build_decode_table(lut, dec_t, a.n_tables, a.max_len);
     __syncthreads();
 
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const uint32_t lane = threadIdx.x % kWave;
     uint8_t *tile = tiles + wave * kTileBytes;
     const uint32_t tile_addr = lds_offset(tile);
-    const uint8_t *lds_count = reinterpret_cast<const uint8_t *>(count_t);
     const uint8_t *lds_dec = reinterpret_cast<const uint8_t *>(dec_t);
 
     // XCD-contiguous assignment: group g runs on XCD g % 8 and takes the
@@ -448,10 +497,12 @@ __global__ __launch_bounds__(kGroupThreads) void df11_decode_kernel(DecodeArgs a
                                  ? (uint32_t)((int64_t)a.total_bits - (int64_t)(g64 * DF11_SLICE_BITS))
                                  : 64u + gap_next;
 
-        // ---- phase 1: count
+        // ---- phase 1: decode into the lane's staging slot, counting
+        const uint32_t slot = tile_addr + kStageBase + lane * kStageStride;
         const uint32_t cnt =
-            lim ? count_codes(lds_count, lut, a.n_tables, d0, d1, d2, pad_ones(d0, (int)end, 0),
-                              pad_ones(d1, (int)end, 32), pad_ones(d2, (int)end, 64), gap, end)
+            lim ? stage_codes(lds_dec, lut, a.n_tables, d0, d1, d2, pad_ones(d0, (int)end, 0),
+                              pad_ones(d1, (int)end, 32), pad_ones(d2, (int)end, 64), gap, lim,
+                              slot, tile_addr + kTileBytes - 4)
                 : 0u;
 
         // wave-wide prefix sum of the counts
@@ -472,13 +523,29 @@ __global__ __launch_bounds__(kGroupThreads) void df11_decode_kernel(DecodeArgs a
         const uint32_t at = (p0 - base) + excl;  // tile position of this lane's first symbol
         const uint32_t stop = lim ? lim : 0u;
         const uint32_t start = lim ? gap : 0u;
+        // every lane's codes fit its slot (then the block fits one tile, too)
+        // and every lane before the last code holds enough for its neighbour
+        const bool last_lane = incl == total;
+        const bool odd = cnt > (uint32_t)kStageCodes || (cnt < (uint32_t)kStageMinCodes && !last_lane);
+        const bool staged = one_pass && __builtin_amdgcn_ballot_w64(odd) == 0;
 
-        if (one_pass) {
-            // ---- phase 2: decode into the tile, then restore each lane's head
+        wave_lds_sync();
+        if (staged) {
+            // ---- move the staged exponents to their tile positions
+            const uint32_t tail = staged_tail(slot, cnt);
+            const uint32_t prev = (uint32_t)__builtin_amdgcn_ds_bpermute(
+                (int)(((lane + kWave - 1) % kWave) * 4), (int)tail);
+            place_staged(slot, tile_addr + at, cnt, prev, last_lane);
+            wave_lds_sync();
+        } else if (one_pass) {
+            // ---- phase 2: decode the real bits again into the tile, then
+            // restore each lane's head
             decode_codes<false>(lds_dec, lut, a.n_tables, d0, d1, d2, start, stop, tile_addr, at, 0);
             wave_lds_sync();
             rewrite_head(lds_dec, lut, a.n_tables, d0, d1, d2, start, cnt, tile_addr + at);
             wave_lds_sync();
+        }
+        if (one_pass) {
             // ---- merge with sign|mantissa, 8 BF16 per lane per 16-byte store
 #pragma unroll
             for (int i = 0; i < kPrefetchGroups; ++i) {
@@ -549,6 +616,9 @@ int launch_groups(int dev, uint32_t n_tables, uint32_t n_blocks, int *groups) {
                                                          lds_bytes(n_tables)) != hipSuccess)
             return DF11_ERR_HIP;
         if (occ <= 0) return DF11_ERR_TABLES;
+#ifdef DF11_MAX_OCCUPANCY
+        occ = occ < DF11_MAX_OCCUPANCY ? occ : DF11_MAX_OCCUPANCY;
+#endif
         g_occ[dev][n_tables].store(occ, std::memory_order_relaxed);
     }
     // a multiple of the XCD count, no more than there are blocks to share
