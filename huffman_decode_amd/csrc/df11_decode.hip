@@ -80,7 +80,6 @@ static_assert(kStageStride % 4 == 0 && kStageBase % 4 == 0 && kTileBytes % 8 == 
 static_assert(kStageStride >= kStageCodes + 4, "a full slot takes 4 stray bytes");
 constexpr int kTableBytes = 256 * 2;
 constexpr int kXcds = 8;
-
 // multi-code decode table (LDS): index width
 constexpr int kDecodeBits = DF11_DECODE_BITS;
 constexpr int kDecodeBytes = (1 << kDecodeBits) * 8;
@@ -88,7 +87,11 @@ constexpr int kMaxSymbolsPerStep = 4;
 constexpr int kTilesBytes = kWavesPerGroup * kTileBytes;
 constexpr int kStaticLds = kTilesBytes + kDecodeBytes;
 static_assert(kTilesBytes < 0x10000, "tile addresses must fit 16 bits");
-constexpr int kPrefetchGroups = 4;  // sign|mantissa groups of 8 per lane loaded up front
+#ifndef DF11_PREFETCH_GROUPS
+#define DF11_PREFETCH_GROUPS 2
+#endif
+// sign|mantissa groups of 8 per lane loaded up front
+constexpr int kPrefetchGroups = DF11_PREFETCH_GROUPS;
 
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 typedef __attribute__((address_space(3))) uint16_t lds_u16;
@@ -201,12 +204,16 @@ __device__ __forceinline__ uint32_t pad_ones(uint32_t d, int end, int base) {
 }
 
 // Phase 1 for one lane: decode the codes starting in [pos, stop) of its slice
-// into its staging slot at LDS address `slot`, four bytes per table step, and
-// return their number.  f* are the slice's dwords with the bits after its last
-// code set to 1 (so a step never runs past that code and the count is exact),
-// d* the plain dwords (for codes longer than the table window).  Stores are
-// clamped to `clamp` so that corrupt input cannot reach past the wave's
-// region; valid data never gets there.
+// into its staging slot at LDS address `slot` (4-aligned) and return their
+// number.  f* are the slice's dwords with the bits after its last code set to
+// 1 (so a step never runs past that code and the count is exact), d* the plain
+// dwords (for codes longer than the table window).
+//
+// Stores are aligned: `cur` holds the slot's partly filled dword, and each
+// step ORs its symbols (unused table bytes are 0) in at the next byte and
+// stores the two dwords they can touch.  Stores are clamped to `clamp` so
+// that corrupt input cannot reach past the wave's region; valid data never
+// gets there.
 __device__ __forceinline__ uint32_t stage_codes(const uint8_t *lds_dec, const uint16_t *lut,
                                                 uint32_t n_tables, uint32_t d0, uint32_t d1,
                                                 uint32_t d2, uint32_t f0, uint32_t f1, uint32_t f2,
@@ -217,24 +224,31 @@ __device__ __forceinline__ uint32_t stage_codes(const uint8_t *lds_dec, const ui
                    e2 = __builtin_amdgcn_alignbit(f2, f1, 29);
     constexpr uint32_t kMask = ((1u << kDecodeBits) - 1) << 3;
     uint32_t acc = pos | (slot << 16);  // pos | (LDS address of the next byte) << 16
+    uint32_t cur = 0;                   // the dword holding that byte, bytes before it
     auto step = [&](uint32_t hi, uint32_t lo, uint32_t dhi, uint32_t dlo) {
         const uint32_t w = __builtin_amdgcn_alignbit(hi, lo, acc);
         const uint2 dv = *reinterpret_cast<const uint2 *>(lds_dec + (w & kMask));
-        uint32_t at = acc >> 16;
-        at = at < clamp ? at : clamp;
-        *(lds_u32 *)(uintptr_t)at = dv.y;
-        uint32_t inc = dv.x;
+        uint32_t inc = dv.x, syms = dv.y;
         if (dv.x < 0x10000u) {  // longer than the window: 8-bit tables, real bits
             const uint32_t e = lookup8(lut, __builtin_amdgcn_alignbit(dhi, dlo, acc), n_tables);
-            *(lds_u8 *)(uintptr_t)at = (uint8_t)e;
+            syms = e & 0xFFu;
             inc = leaf_len(e) | 0x10000u;
         }
+        uint32_t at = acc >> 16;
+        at = at < clamp ? at : clamp;
+        const uint64_t t = (uint64_t)syms << ((at & 3u) * 8u);
+        const uint32_t w0 = cur | (uint32_t)t, w1 = (uint32_t)(t >> 32);
+        lds_u32 *p = (lds_u32 *)(uintptr_t)(at & ~3u);
+        p[0] = w0;
+        p[1] = w1;
         acc += inc;
+        cur = ((acc >> 16) ^ at) & ~3u ? w1 : w0;
     };
+    // every step moves at least one bit on (table entries and 8-bit leaves
+    // have lengths >= 1), so a lane takes at most 64 steps, whatever the data
     const uint32_t stop0 = stop < 32u ? stop : 32u;
-    // a half holds at most 32 code starts: the bound only matters for corrupt input
-    for (int it = 0; it < 32 && (acc & 0xFFFFu) < stop0; ++it) step(e1, e0, d1, d0);
-    for (int it = 0; it < 32 && (acc & 0xFFFFu) < stop; ++it) step(e2, e1, d2, d1);
+    while ((acc & 0xFFFFu) < stop0) step(e1, e0, d1, d0);
+    while ((acc & 0xFFFFu) < stop) step(e2, e1, d2, d1);
     return (acc >> 16) - slot;
 }
 
@@ -334,8 +348,8 @@ __device__ __forceinline__ void decode_codes(const uint8_t *lds_dec, const uint1
             }
         }
     };
-    for (int it = 0; it < 32 && (acc & 0xFFFFu) < stop0; ++it) step(e1, e0, d1, d0);
-    for (int it = 0; it < 32 && (acc & 0xFFFFu) < stop; ++it) step(e2, e1, d2, d1);
+    while ((acc & 0xFFFFu) < stop0) step(e1, e0, d1, d0);  // at most 64 steps, as above
+    while ((acc & 0xFFFFu) < stop) step(e2, e1, d2, d1);
 }
 
 // After every lane's unranged decode: store this lane's first min(3, cnt)
@@ -377,11 +391,12 @@ __device__ __forceinline__ uint32_t join1(uint32_t e, uint32_t sm) {
     return ((sm & 0x80u) << 8) | ((e & 0xFFu) << 7) | (sm & 0x7Fu);
 }
 
-#ifdef DF11_WAVES_PER_EU
-#define DF11_OCCUPANCY_HINT __attribute__((amdgpu_waves_per_eu(DF11_WAVES_PER_EU)))
-#else
-#define DF11_OCCUPANCY_HINT
+// at least 6 waves per SIMD: keeps the register budget at 80 VGPRs, the
+// most that still lets 3 workgroups of 8 waves share a CU
+#ifndef DF11_WAVES_PER_EU
+#define DF11_WAVES_PER_EU 6
 #endif
+#define DF11_OCCUPANCY_HINT __attribute__((amdgpu_waves_per_eu(DF11_WAVES_PER_EU)))
 __global__ __launch_bounds__(kGroupThreads) DF11_OCCUPANCY_HINT void df11_decode_kernel(DecodeArgs a) {
     // LDS: per-wave regions (staging slots, then the exponent tile) | decode
     // table in one static array (fixed offsets fold into the ds_read/ds_write
@@ -449,6 +464,16 @@ __global__ __launch_bounds__(kGroupThreads) DF11_OCCUPANCY_HINT void df11_decode
             bp_hi = mine < range_hi ? a.block_pos[mine + 1] : 0u;
             asm volatile("" ::"v"(bp_lo), "v"(bp_hi));  // waited here, not behind stores
         }
+        // Rotate the wave's issue priority from block to block.  At equal
+        // priority a SIMD issues the oldest wave first, so with fixed shares of
+        // blocks the youngest workgroups of a CU finish far behind the oldest;
+        // rotating priorities spreads that preference over all waves.
+        switch ((k + wave + slot) & 3u) {
+        case 0: __builtin_amdgcn_s_setprio(0); break;
+        case 1: __builtin_amdgcn_s_setprio(1); break;
+        case 2: __builtin_amdgcn_s_setprio(2); break;
+        default: __builtin_amdgcn_s_setprio(3); break;
+        }
         const uint32_t p0 = __builtin_amdgcn_readlane(bp_lo, k & 63);
         const uint32_t p1 = __builtin_amdgcn_readlane(bp_hi, k & 63);
         const uint32_t d0 = nd0, d1 = nd1, d2 = nd2, gw0 = ng0, gw1 = ng1;
@@ -487,14 +512,21 @@ __global__ __launch_bounds__(kGroupThreads) DF11_OCCUPANCY_HINT void df11_decode
 
         const uint32_t gw = __builtin_amdgcn_alignbit(gw1, gw0, gap_shift);
         const uint32_t gap = gw & 31u, gap_next = (gw >> 5) & 31u;
-        const uint64_t g64 = (uint64_t)b * DF11_BLOCK_SLICES + lane;
-        const int64_t rel = (int64_t)a.stop_bit - (int64_t)(g64 * DF11_SLICE_BITS);
+        // the stop bit and the stream end relative to this lane's slice, in
+        // 32 bits: wave-uniform 64-bit differences to the block start,
+        // clamped far outside the block's 4096 bits, minus the lane's offset
+        const uint64_t blk_bit = (uint64_t)b * (DF11_BLOCK_SLICES * DF11_SLICE_BITS);
+        auto near = [](int64_t v) {
+            return (int32_t)(v < -(1 << 30) ? -(1 << 30) : (v > (1 << 30) ? (1 << 30) : v));
+        };
+        const int32_t lane_bit = (int32_t)(lane * DF11_SLICE_BITS);
+        const int32_t rel = near((int64_t)a.stop_bit - (int64_t)blk_bit) - lane_bit;
         // codes of this lane start in [gap, lim); the last one ends at `end`:
         // the next slice's first code start, or the stream's end for the lane
         // holding the final code
         const uint32_t lim = rel <= 0 ? 0u : (rel >= 64 ? 64u : (uint32_t)rel);
         const uint32_t end = rel > 0 && rel <= 64
-                                 ? (uint32_t)((int64_t)a.total_bits - (int64_t)(g64 * DF11_SLICE_BITS))
+                                 ? (uint32_t)(near((int64_t)a.total_bits - (int64_t)blk_bit) - lane_bit)
                                  : 64u + gap_next;
 
         // ---- phase 1: decode into the lane's staging slot, counting
@@ -502,7 +534,7 @@ __global__ __launch_bounds__(kGroupThreads) DF11_OCCUPANCY_HINT void df11_decode
         const uint32_t cnt =
             lim ? stage_codes(lds_dec, lut, a.n_tables, d0, d1, d2, pad_ones(d0, (int)end, 0),
                               pad_ones(d1, (int)end, 32), pad_ones(d2, (int)end, 64), gap, lim,
-                              slot, tile_addr + kTileBytes - 4)
+                              slot, tile_addr + kTileBytes - 8)
                 : 0u;
 
         // wave-wide prefix sum of the counts
