@@ -404,6 +404,8 @@ __global__ __launch_bounds__(kGroupThreads) DF11_OCCUPANCY_HINT void df11_decode
     // addresses fit the 16-bit field of the phase accumulators), then the 8-bit
     // tables in dynamic LDS.
     __shared__ __attribute__((aligned(16))) uint8_t lds_static[kStaticLds];
+    __shared__ uint32_t wg_next;  // next block index of this workgroup's share
+    if (threadIdx.x == 0) wg_next = 0;
     uint8_t *tiles = lds_static;
     uint2 *dec_t = reinterpret_cast<uint2 *>(lds_static + kTilesBytes);
     extern __shared__ uint4 smem_u4[];
@@ -427,8 +429,9 @@ __global__ __launch_bounds__(kGroupThreads) DF11_OCCUPANCY_HINT void df11_decode
     const uint32_t tile_addr = lds_offset(tile);
     const uint8_t *lds_dec = reinterpret_cast<const uint8_t *>(dec_t);
 
-    // XCD-contiguous assignment: group g runs on XCD g % 8 and takes the
-    // blocks of that XCD's range with a stride of (groups per XCD * waves)
+    // XCD-contiguous assignment: group g runs on XCD g % 8 (workgroups are
+    // dispatched round-robin over the XCDs) and owns the blocks
+    // range_lo + 8 slot + {0..7} + i * stride of that XCD's range.
     const uint32_t xcd = blockIdx.x % kXcds;
     const uint32_t slot = blockIdx.x / kXcds;
     const uint32_t groups_per_xcd = gridDim.x / kXcds;
@@ -436,7 +439,6 @@ __global__ __launch_bounds__(kGroupThreads) DF11_OCCUPANCY_HINT void df11_decode
     uint32_t range_hi = range_lo + a.blocks_per_xcd;
     range_hi = range_hi < a.n_blocks ? range_hi : a.n_blocks;
     const uint32_t stride = groups_per_xcd * kWavesPerGroup;
-    const uint32_t first = range_lo + slot * kWavesPerGroup + wave;
 
     // slice g = 64 b + lane: its stream dwords are 2g..2g+2 and its 5-bit
     // gap field sits at bit 5 * lane of the block's 320 gap bits (dword 10 b)
@@ -444,44 +446,54 @@ __global__ __launch_bounds__(kGroupThreads) DF11_OCCUPANCY_HINT void df11_decode
     auto gaps_at = [&](uint32_t blk) { return a.gaps + 10 * blk + ((5 * lane) >> 5); };
     const uint32_t gap_shift = (5 * lane) & 31;
 
-    // block output positions of the wave's next 64 blocks: lane k holds block k's
-    uint32_t bp_lo = 0, bp_hi = 0;
-    uint32_t nd0 = 0, nd1 = 0, nd2 = 0, ng0 = 0, ng1 = 0;
-    if (first < range_hi) {
-        const uint32_t *sp = stream_at(first);
+    // The workgroup's blocks go to its waves one at a time through an LDS
+    // counter, claimed a block ahead, so a wave that the SIMD serves less
+    // often simply takes fewer blocks.  (Workgroups keep fixed shares: global
+    // atomics would queue every wave of an XCD on one address.)
+    auto wg_block = [&](uint32_t i) {
+        const uint32_t blk = range_lo + slot * kWavesPerGroup + (i % kWavesPerGroup) +
+                             (i / kWavesPerGroup) * stride;
+        return blk < range_hi ? blk : 0xFFFFFFFFu;
+    };
+    auto claim = [&]() {
+        uint32_t v = 0;
+        if (lane == 0) v = atomicAdd(&wg_next, 1u);
+        return v;
+    };
+    uint32_t b = wg_block(__builtin_amdgcn_readfirstlane(claim()));
+    uint32_t nb = b != 0xFFFFFFFFu ? wg_block(__builtin_amdgcn_readfirstlane(claim())) : 0xFFFFFFFFu;
+    uint32_t nd0 = 0, nd1 = 0, nd2 = 0, ng0 = 0, ng1 = 0, npos = 0;
+    if (b != 0xFFFFFFFFu) {
+        const uint32_t *sp = stream_at(b);
         nd0 = sp[0], nd1 = sp[1], nd2 = sp[2];
-        const uint32_t *gp = gaps_at(first);
+        const uint32_t *gp = gaps_at(b);
         ng0 = gp[0], ng1 = gp[1];
+        npos = a.block_pos[b + (lane & 1)];
     }
-    // waited before the loop so that the loop header needs no wait (a wait
-    // there would also cover the previous block's stores)
-    asm volatile("" ::"v"(nd0), "v"(nd1), "v"(nd2), "v"(ng0), "v"(ng1));
+    asm volatile("" ::"v"(nd0), "v"(nd1), "v"(nd2), "v"(ng0), "v"(ng1), "v"(npos));
     uint32_t k = 0;
-    for (uint32_t b = first; b < range_hi; b += stride, ++k) {
-        if ((k & 63) == 0) {
-            const uint32_t mine = b + lane * stride;
-            bp_lo = mine < range_hi ? a.block_pos[mine] : 0u;
-            bp_hi = mine < range_hi ? a.block_pos[mine + 1] : 0u;
-            asm volatile("" ::"v"(bp_lo), "v"(bp_hi));  // waited here, not behind stores
-        }
+    while (b != 0xFFFFFFFFu) {
         // Rotate the wave's issue priority from block to block.  At equal
         // priority a SIMD issues the oldest wave first, so with fixed shares of
-        // blocks the youngest workgroups of a CU finish far behind the oldest;
-        // rotating priorities spreads that preference over all waves.
+        // blocks the youngest workgroups of a CU would finish far behind the
+        // oldest; rotating priorities spreads that preference over all waves.
         switch ((k + wave + slot) & 3u) {
         case 0: __builtin_amdgcn_s_setprio(0); break;
         case 1: __builtin_amdgcn_s_setprio(1); break;
         case 2: __builtin_amdgcn_s_setprio(2); break;
         default: __builtin_amdgcn_s_setprio(3); break;
         }
-        const uint32_t p0 = __builtin_amdgcn_readlane(bp_lo, k & 63);
-        const uint32_t p1 = __builtin_amdgcn_readlane(bp_hi, k & 63);
+        const uint32_t p0 = __builtin_amdgcn_readlane(npos, 0);
+        const uint32_t p1 = __builtin_amdgcn_readlane(npos, 1);
         const uint32_t d0 = nd0, d1 = nd1, d2 = nd2, gw0 = ng0, gw1 = ng1;
-        if (b + stride < range_hi) {  // the next block's inputs, consumed next iteration
-            const uint32_t *sp = stream_at(b + stride);
+        uint32_t pend = 0;
+        if (nb != 0xFFFFFFFFu) {
+            const uint32_t *sp = stream_at(nb);
             nd0 = sp[0], nd1 = sp[1], nd2 = sp[2];
-            const uint32_t *gp = gaps_at(b + stride);
+            const uint32_t *gp = gaps_at(nb);
             ng0 = gp[0], ng1 = gp[1];
+            npos = a.block_pos[nb + (lane & 1)];
+            pend = claim();
         }
         const bool sane = p1 >= p0 && p1 <= a.n && p1 - p0 <= (uint32_t)kMaxBlockCodes;
         const uint32_t base = p0 & ~7u;
@@ -545,7 +557,14 @@ __global__ __launch_bounds__(kGroupThreads) DF11_OCCUPANCY_HINT void df11_decode
         // for the next block's prefetched inputs here, on every path and before
         // this block's stores are issued, so that no later wait (the loop
         // header's in particular) has to cover those stores
-        asm volatile("" ::"v"(nd0), "v"(nd1), "v"(nd2), "v"(ng0), "v"(ng1));
+        asm volatile("" ::"v"(nd0), "v"(nd1), "v"(nd2), "v"(ng0), "v"(ng1), "v"(npos));
+        {
+            const uint32_t nnb = nb != 0xFFFFFFFFu ? wg_block(__builtin_amdgcn_readfirstlane(pend))
+                                                   : 0xFFFFFFFFu;
+            b = nb;  // the rest of this iteration only uses p0, p1 and the lanes' data
+            nb = nnb;
+            ++k;
+        }
         // a count that disagrees with block_pos means a corrupt block: report
         // it and leave its output unwritten
         if (!sane || total != p1 - p0) {
