@@ -236,7 +236,8 @@ __device__ __forceinline__ uint32_t stage_codes(const uint8_t *lds_dec, const ui
         }
         uint32_t at = acc >> 16;
         at = at < clamp ? at : clamp;
-        const uint64_t t = (uint64_t)syms << ((at & 3u) * 8u);
+        // bits 13..17 of acc: pos >> 13 (always 0) | (byte address & 3) << 3
+        const uint64_t t = (uint64_t)syms << __builtin_amdgcn_ubfe(acc, 13, 5);
         const uint32_t w0 = cur | (uint32_t)t, w1 = (uint32_t)(t >> 32);
         lds_u32 *p = (lds_u32 *)(uintptr_t)(at & ~3u);
         p[0] = w0;
