@@ -143,6 +143,76 @@ def gemm_ratios(wlx, out, decode_ms, stream, batches=(1, 64), reps=10) -> dict:
     return res
 
 
+def run_stack(args) -> int:
+    """The 32-block Llama-3.1-8B-shaped stack: each block decoded into a reused
+    BF16 buffer, then its 7 bf16 GEMMs at batch 1 and 64.  Reports the time of
+    one forward pass (all blocks) for the decodes alone, the GEMMs alone on
+    resident BF16 weights, decode+GEMMs on one stream, and decode of block i+1
+    overlapped with the GEMMs of block i on two streams; and their ratios."""
+    import numpy as np
+    import torch
+    import huffman_decode_amd as hd
+    from huffman_decode_amd import workloads as wl
+    from huffman_decode_amd.pipeline import StackBlock, StackRunner
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    blocks, resident, exact, t_enc = [], [], True, 0.0
+    for layer in range(args.layers):
+        wlx = wl.llama8b_stack_block(layer)
+        t0 = time.perf_counter()
+        enc = hd.encode(wlx.weights)
+        t_enc += time.perf_counter() - t0
+        d = hd.to_device(enc, dev)
+        shapes = [(m.rows, m.cols) for m in wlx.matrices]
+        blocks.append(StackBlock(d, shapes))
+        # the decoded copy doubles as the resident BF16 weights of the GEMM-only pass
+        buf = torch.empty(enc.n, dtype=torch.bfloat16, device=dev)
+        hd.df11_decode(d, buf)
+        orig = torch.from_numpy(wlx.weights.view(np.int16)).to(dev)
+        exact &= bool(torch.equal(buf.view(torch.int16), orig))
+        resident.append(buf)
+        del orig, wlx, enc
+        print(f"[stack] layer {layer} encoded and checked", file=sys.stderr, flush=True)
+    runner = StackRunner(blocks, dev)
+    cs = runner.compute_stream
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(cs)
+        for _ in range(reps):
+            fn()
+        e1.record(cs)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    res = {}
+    for batch in (1, 64):
+        acts, outs = runner.activations(batch)
+        t_dec = timed(runner.run_decodes_only, args.steps)
+        t_gemm = timed(lambda: runner.run_gemms_only(acts, outs, resident), args.steps)
+        t_ser = timed(lambda: runner.run_serial(acts, outs), args.steps)
+        t_ovl = {g: timed(lambda: runner.run_overlapped(acts, outs, g), args.steps)
+                 for g in (0, 512, 384, 256)}
+        best = min(t_ovl, key=t_ovl.get)
+        res[f"batch{batch}"] = {
+            "forward_ms": {"decode_only": round(t_dec, 4), "bf16_gemm_only": round(t_gemm, 4),
+                           "df11_serial": round(t_ser, 4),
+                           "df11_overlapped_by_decode_groups": {str(g): round(t, 4)
+                                                                for g, t in t_ovl.items()}},
+            "decode_over_gemm": round(t_dec / t_gemm, 4),
+            "df11_serial_over_bf16": round(t_ser / t_gemm, 4),
+            "df11_overlapped_over_bf16": round(t_ovl[best] / t_gemm, 4),
+            "overlap_decode_groups": best}
+    n = sum(b.dev.n for b in blocks)
+    print(json.dumps({"mode": "stack", "workload": "llama8b_stack", "layers": args.layers,
+                      "n_weights": n, "bit_exact": exact, "host_encode_s": round(t_enc, 2),
+                      "reps": args.steps, **res}), flush=True)
+    return 0 if exact else 1
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -153,8 +223,10 @@ def main() -> int:
                     help="rotating encoded copies (defeats the Infinity Cache)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-gemm", action="store_true", help="skip the decode/GEMM ratios")
-    ap.add_argument("--mode", choices=("decode", "copy"), default="decode",
-                    help="copy: time a plain device copy of --copy-mib MiB instead")
+    ap.add_argument("--mode", choices=("decode", "copy", "stack"), default="decode",
+                    help="copy: time a plain device copy of --copy-mib MiB instead; "
+                         "stack: decode/GEMM schedules over the 32-block 8B-shaped stack")
+    ap.add_argument("--layers", type=int, default=32, help="blocks in the stack mode")
     ap.add_argument("--copy-mib", type=int, default=1024)
     args = ap.parse_args()
 
@@ -166,6 +238,8 @@ def main() -> int:
 
     if args.mode == "copy":
         return run_copy(args)
+    if args.mode == "stack":
+        return run_stack(args)
 
     import numpy as np
     import torch

@@ -57,7 +57,7 @@ class DeviceStream(ctypes.Structure):
                 ("stream_bytes", _U64), ("gaps_bytes", _U64), ("block_pos_count", _U64),
                 ("signmant_bytes", _U64), ("lut_bytes", _U64), ("n", _U64),
                 ("total_bits", _U64), ("last_start", _U64), ("n_blocks", _U32),
-                ("n_tables", _U32), ("max_len", _U32), ("reserved", _U32), ("status", _P)]
+                ("n_tables", _U32), ("max_len", _U32), ("max_groups", _U32), ("status", _P)]
 
 
 class Df11Error(RuntimeError):

@@ -644,7 +644,8 @@ std::atomic<int> g_occ[kMaxDevices][DF11_MAX_TABLES + 1];
 // dynamic LDS per workgroup: the 8-bit tables (tiles and fast tables are static)
 size_t lds_bytes(uint32_t n_tables) { return (size_t)n_tables * kTableBytes; }
 
-int launch_groups(int dev, uint32_t n_tables, uint32_t n_blocks, int *groups) {
+int launch_groups(int dev, uint32_t n_tables, uint32_t n_blocks, uint32_t max_groups,
+                  int *groups) {
     if (dev < 0 || dev >= kMaxDevices) return DF11_ERR_HIP;
     int cus = g_cus[dev].load(std::memory_order_relaxed);
     if (cus <= 0) {
@@ -676,6 +677,10 @@ int launch_groups(int dev, uint32_t n_tables, uint32_t n_blocks, int *groups) {
     // a multiple of the XCD count, no more than there are blocks to share
     const uint64_t want = ((uint64_t)n_blocks + kWavesPerGroup - 1) / kWavesPerGroup;
     uint64_t cap = (uint64_t)cus * (uint64_t)occ;
+    if (max_groups) {
+        const uint64_t lim = max_groups < (uint32_t)kXcds ? kXcds : max_groups / kXcds * kXcds;
+        cap = cap < lim ? cap : lim;
+    }
     uint64_t g = want < cap ? want : cap;
     g = (g + kXcds - 1) / kXcds * kXcds;
     *groups = (int)g;
@@ -709,7 +714,7 @@ extern "C" int df11_decode(const df11_device_stream *s, uint16_t *out, void *hip
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return DF11_ERR_HIP;
     int groups = 0;
-    int st = launch_groups(dev, s->n_tables, s->n_blocks, &groups);
+    int st = launch_groups(dev, s->n_tables, s->n_blocks, s->max_groups, &groups);
     if (st != DF11_OK) return st;
 
     DecodeArgs a;

@@ -1,0 +1,130 @@
+"""Decode-then-GEMM scheduling over a stack of DF11 transformer blocks.
+
+The DF11 pages describe inference that decompresses each transformer block's
+weights just before its matrix products and discards them afterwards (page
+"DFloat11: lossless BFloat16 compression", section "Architecture").  This
+module runs that pattern on one GPU, with the decode and the consumer GEMMs
+(``y = x W^T`` for each matrix of a block, torch bf16 matmuls) either on one
+stream (serial) or overlapped: block i+1 is decoded on a second stream into
+the other half of a double buffer while block i's GEMMs run.  Device memory
+holds the compressed blocks plus two BF16 buffers of the largest block.
+
+Only stream/event ordering lives here; every decode is a ``df11_decode``
+launch of the native library.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+from . import DeviceEncoded, df11_decode
+
+
+@dataclass
+class StackBlock:
+    """One encoded transformer block and the (rows, cols) of its matrices in
+    storage order (row-major, concatenated)."""
+    dev: DeviceEncoded
+    shapes: list[tuple[int, int]]
+
+
+class StackRunner:
+    """Runs ``decode(block i) -> GEMMs(block i)`` for a list of blocks."""
+
+    def __init__(self, blocks: list[StackBlock], device="cuda"):
+        import torch
+        if not blocks:
+            raise ValueError("no blocks")
+        self.blocks = blocks
+        self.device = torch.device(device)
+        n_max = max(b.dev.n for b in blocks)
+        for b in blocks:
+            if sum(r * c for r, c in b.shapes) != b.dev.n:
+                raise ValueError("matrix shapes do not cover the block's weights")
+        # two decode targets: block i uses buffer i % 2
+        self.buffers = [torch.empty(n_max, dtype=torch.bfloat16, device=self.device)
+                        for _ in range(2)]
+        self.decode_stream = torch.cuda.Stream(device=self.device)
+        self.compute_stream = torch.cuda.current_stream(self.device)
+
+    @staticmethod
+    def _views(buf, shapes):
+        out, off = [], 0
+        for r, c in shapes:
+            out.append(buf[off: off + r * c].view(r, c))
+            off += r * c
+        return out
+
+    def _gemms(self, i, buf, acts, outs):
+        """Block i's GEMMs on the weights in buf.  ``outs`` is one dict of
+        outputs by matrix shape shared by all blocks, or a list of such dicts,
+        one per block."""
+        import torch
+        shapes = self.blocks[i].shapes
+        o = outs[i] if isinstance(outs, list) else outs
+        for w, sh in zip(self._views(buf, shapes), shapes):
+            torch.matmul(acts[sh], w.t(), out=o[sh])
+
+    def activations(self, batch: int, seed: int = 3999, per_block: bool = False):
+        """One bf16 activation [batch, cols] per matrix shape (N(0,1) from a
+        seeded generator) and outputs [batch, rows]: one dict by shape, or with
+        per_block a list of such dicts, one per block."""
+        import torch
+        g = torch.Generator(device=self.device).manual_seed(seed)
+        shapes = sorted({s for b in self.blocks for s in b.shapes})
+        acts = {(r, c): torch.randn(batch, c, generator=g, device=self.device).to(torch.bfloat16)
+                for r, c in shapes}
+
+        def new_outs():
+            return {(r, c): torch.empty(batch, r, dtype=torch.bfloat16, device=self.device)
+                    for r, c in shapes}
+        return acts, ([new_outs() for _ in self.blocks] if per_block else new_outs())
+
+    def run_serial(self, acts, outs):
+        """Decode and GEMMs of every block in order on the compute stream."""
+        s = self.compute_stream
+        for i, blk in enumerate(self.blocks):
+            buf = self.buffers[i % 2]
+            df11_decode(blk.dev, buf, s)
+            self._gemms(i, buf, acts, outs)
+
+    def run_overlapped(self, acts, outs, decode_groups: int = 0):
+        """Decode of block i+1 (decode stream) overlaps the GEMMs of block i
+        (compute stream).  Buffer i % 2 is reused by block i + 2 only after
+        block i's GEMMs are done.  Work is enqueued in block order, so every
+        event is recorded before a stream is told to wait for it (a wait on
+        an event not yet recorded would not wait at all).  ``decode_groups``
+        (0 = all that fit) caps the decode's workgroups, leaving compute units
+        to the GEMMs."""
+        import torch
+        ds, cs = self.decode_stream, self.compute_stream
+        n = len(self.blocks)
+        decoded = [torch.cuda.Event() for _ in range(n)]
+        consumed = [torch.cuda.Event() for _ in range(n)]
+        for blk in self.blocks:
+            blk.dev.desc.max_groups = decode_groups
+        ds.wait_stream(cs)  # inputs prepared on the compute stream
+        df11_decode(self.blocks[0].dev, self.buffers[0], ds)
+        decoded[0].record(ds)
+        for i, blk in enumerate(self.blocks):
+            if i + 1 < n:
+                if i >= 1:
+                    ds.wait_event(consumed[i - 1])  # block i+1 reuses block i-1's buffer
+                df11_decode(self.blocks[i + 1].dev, self.buffers[(i + 1) % 2], ds)
+                decoded[i + 1].record(ds)
+            cs.wait_event(decoded[i])
+            self._gemms(i, self.buffers[i % 2], acts, outs)
+            consumed[i].record(cs)
+        cs.wait_stream(ds)
+        for blk in self.blocks:
+            blk.dev.desc.max_groups = 0
+
+    def run_gemms_only(self, acts, outs, resident):
+        """The BF16 reference: the same GEMMs on already resident BF16 weights
+        (``resident[i]`` holds block i's decoded weights)."""
+        for i, buf in enumerate(resident):
+            self._gemms(i, buf, acts, outs)
+
+    def run_decodes_only(self):
+        s = self.compute_stream
+        for i, blk in enumerate(self.blocks):
+            df11_decode(blk.dev, self.buffers[i % 2], s)

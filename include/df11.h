@@ -145,7 +145,10 @@ typedef struct df11_device_stream {
     uint64_t n, total_bits, last_start;
     uint32_t n_blocks, n_tables;
     uint32_t max_len;  /* longest code of the code book (1..32) */
-    uint32_t reserved;
+    uint32_t max_groups; /* 0: launch as many workgroups as fit on the GPU at
+                            once; otherwise at most this many (rounded down to
+                            a multiple of 8, at least 8), leaving compute units
+                            to kernels that run alongside on other streams */
     uint32_t *status;  /* optional device word; each block whose decoded
                           count differs from its block_pos range, or whose
                           block_pos range is malformed, adds 1 (the block's

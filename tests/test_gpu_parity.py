@@ -127,3 +127,28 @@ def test_gemm_bit_exact_after_decode(torch):
         y1 = torch.matmul(x, w_dec.t())
         torch.cuda.synchronize()
         assert torch.equal(y0, y1)
+
+
+def test_stack_pipeline_overlapped_matches_bf16_gemms(torch):
+    """Decode-then-GEMM over a small stack: serial and overlapped schedules
+    give, block by block, the same GEMM outputs as the GEMMs on the original
+    BF16 weights (same matmuls on bit-identical inputs)."""
+    from huffman_decode_amd.pipeline import StackBlock, StackRunner
+    blocks, originals = [], []
+    for layer in range(4):
+        w = wl.llama8b_block(seed=(3001, layer), scale=1 / 64)
+        enc = hd.encode(w.weights)
+        blocks.append(StackBlock(hd.to_device(enc), [(m.rows, m.cols) for m in w.matrices]))
+        originals.append(torch.from_numpy(w.weights.view(np.int16)).cuda().view(torch.bfloat16))
+    runner = StackRunner(blocks)
+    for batch in (1, 64):
+        acts, ref = runner.activations(batch, per_block=True)
+        runner.run_gemms_only(acts, ref, originals)
+        for mode in ("serial", "overlapped"):
+            _say(f"[gpu] stack pipeline {mode} batch={batch}")
+            _, outs = runner.activations(batch, per_block=True)
+            getattr(runner, f"run_{mode}")(acts, outs)
+            torch.cuda.synchronize()
+            for i in range(len(blocks)):
+                for sh in ref[i]:
+                    assert torch.equal(outs[i][sh], ref[i][sh]), (mode, batch, i, sh)
