@@ -213,6 +213,42 @@ def run_stack(args) -> int:
     return 0 if exact else 1
 
 
+def run_encode(args) -> int:
+    """Host encoder throughput: histogram, code book, tables and encoded arrays
+    of one transformer block (df11_encode and its helpers, no GPU), with all
+    hardware threads and with one, next to the single-thread per-block times
+    the DF11 pages report for their Python compressor (191 s for an 8B block,
+    547 s for a 70B block)."""
+    import numpy as np
+    import huffman_decode_amd as hd
+    from huffman_decode_amd import workloads as wl
+    import oracle
+    pages_s = {"llama8b_block": 191.0, "llama70b_block": 547.0}
+    out = {"mode": "encode", "host_threads": os.cpu_count(), "blocks": {}}
+    ok = True
+    for name in ("llama8b_block", "llama70b_block"):
+        wlx = wl.CONFIGS[name]()
+        row = {"n_weights": wlx.n, "pages_single_thread_s": pages_s[name]}
+        for threads in (0, 1):
+            t0 = time.perf_counter()
+            enc = hd.encode(wlx.weights, n_threads=threads)
+            dt = time.perf_counter() - t0
+            key = "all_threads" if threads == 0 else "one_thread"
+            row[key] = {"seconds": round(dt, 3), "gweights_per_s": round(wlx.n / dt / 1e9, 4),
+                        "speedup_vs_pages": round(pages_s[name] / dt, 1)}
+        # the encoding must be the oracle's, byte for byte, on a sample of it
+        row["code_plus_signmant_bits_per_weight"] = round(8 + enc.sizes.total_bits / enc.n, 4)
+        k = min(enc.n, 1 << 22)
+        ref = oracle.encode(wlx.weights[:k])
+        same = bool(np.array_equal(hd.encode(wlx.weights[:k]).stream[:ref.stream.size], ref.stream))
+        row["matches_oracle_on_first_4M"] = same
+        ok &= same
+        out["blocks"][name] = row
+        print(f"[encode] {name} done", file=sys.stderr, flush=True)
+    print(json.dumps(out), flush=True)
+    return 0 if ok else 1
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -223,9 +259,10 @@ def main() -> int:
                     help="rotating encoded copies (defeats the Infinity Cache)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-gemm", action="store_true", help="skip the decode/GEMM ratios")
-    ap.add_argument("--mode", choices=("decode", "copy", "stack"), default="decode",
+    ap.add_argument("--mode", choices=("decode", "copy", "stack", "encode"), default="decode",
                     help="copy: time a plain device copy of --copy-mib MiB instead; "
-                         "stack: decode/GEMM schedules over the 32-block 8B-shaped stack")
+                         "stack: decode/GEMM schedules over the 32-block 8B-shaped stack; "
+                         "encode: host encoder throughput (no GPU)")
     ap.add_argument("--layers", type=int, default=32, help="blocks in the stack mode")
     ap.add_argument("--copy-mib", type=int, default=1024)
     args = ap.parse_args()
@@ -240,6 +277,8 @@ def main() -> int:
         return run_copy(args)
     if args.mode == "stack":
         return run_stack(args)
+    if args.mode == "encode":
+        return run_encode(args)
 
     import numpy as np
     import torch
