@@ -249,6 +249,33 @@ def run_encode(args) -> int:
     return 0 if ok else 1
 
 
+def fused_gemv(wlx, copies, stream, reps=20) -> dict:
+    """Batch-1 y = W x straight from the DF11 stream (df11_decode_gemv, no BF16
+    weights in memory), timed per launch pair like the decode."""
+    import numpy as np
+    import torch
+    import huffman_decode_amd as hd
+    shapes = [(m.rows, m.cols) for m in wlx.matrices]
+    mats, nx, ny = hd.gemv_matrices(shapes)
+    dev0 = copies[0]
+    x = torch.from_numpy(np.random.default_rng(7).standard_normal(nx).astype(np.float32)).cuda()
+    x = x.to(torch.bfloat16)
+    y = torch.empty(ny, dtype=torch.float32, device="cuda")
+    ws = torch.empty(hd.df11_gemv_workspace_bytes(dev0), dtype=torch.uint8, device="cuda")
+    for k in range(3):
+        hd.df11_decode_gemv(copies[k % len(copies)], mats, x, y, ws, stream)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    for k, (a, b) in enumerate(ev):
+        a.record(stream)
+        hd.df11_decode_gemv(copies[k % len(copies)], mats, x, y, ws, stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = sum(a.elapsed_time(b) for a, b in ev) / reps
+    return {"fused_ms": round(ms, 5)}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -355,6 +382,9 @@ def main() -> int:
     }
     if not args.no_gemm:
         line["decode_vs_gemm"] = gemm_ratios(wlx, out, avg_ms, stream)
+        fg = fused_gemv(wlx, copies, stream)
+        fg["fused_over_bf16_gemv"] = round(fg["fused_ms"] / line["decode_vs_gemm"]["batch1"]["gemm_ms"], 4)
+        line["decode_vs_gemm"]["batch1_fused_decode_gemv"] = fg
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wlx, enc)
     print(json.dumps(line), flush=True)

@@ -52,6 +52,11 @@ class Sizes(ctypes.Structure):
                 ("lut_bytes", _U64), ("n_blocks", _U32), ("reserved", _U32)]
 
 
+class GemvMatrix(ctypes.Structure):
+    _fields_ = [("offset", _U64), ("rows", _U32), ("cols", _U32), ("x_offset", _U32),
+                ("y_offset", _U32)]
+
+
 class DeviceStream(ctypes.Structure):
     _fields_ = [("stream", _P), ("gaps", _P), ("block_pos", _P), ("signmant", _P), ("luts", _P),
                 ("stream_bytes", _U64), ("gaps_bytes", _U64), ("block_pos_count", _U64),
@@ -89,6 +94,12 @@ def _load():
         for fn in ("df11_histogram", "df11_build_codebook", "df11_build_luts",
                    "df11_encoded_sizes", "df11_encode", "df11_decode"):
             getattr(lib, fn).restype = ctypes.c_int
+        if hasattr(lib, "df11_decode_gemv"):
+            lib.df11_gemv_workspace_bytes.argtypes = [ctypes.POINTER(DeviceStream)]
+            lib.df11_gemv_workspace_bytes.restype = _U64
+            lib.df11_decode_gemv.argtypes = [ctypes.POINTER(DeviceStream),
+                                             ctypes.POINTER(GemvMatrix), _U32, _P, _P, _P, _U64, _P]
+            lib.df11_decode_gemv.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -261,3 +272,45 @@ def decode(dev: DeviceEncoded, out=None, stream=None):
         out = torch.empty(dev.n, dtype=torch.bfloat16, device=dev.tensors["stream"].device)
     df11_decode(dev, out, stream)
     return out
+
+
+# ------------------------------------------------------------ fused GEMV
+
+GEMV_MAX_MATRICES = 16
+GEMV_MIN_COLS = 2048
+
+
+def gemv_matrices(shapes: list[tuple[int, int]]) -> tuple[list[GemvMatrix], int, int]:
+    """Matrix list for row-major [rows, cols] matrices laid end to end, each
+    with its own slice of x and y (x slices 8-aligned).  Returns (matrices,
+    x length, y length)."""
+    mats, off, xo, yo = [], 0, 0, 0
+    for r, c in shapes:
+        mats.append(GemvMatrix(off, r, c, xo, yo))
+        off += r * c
+        xo += (c + 7) // 8 * 8
+        yo += r
+    return mats, xo, yo
+
+
+def df11_gemv_workspace_bytes(dev: DeviceEncoded) -> int:
+    return int(_load().df11_gemv_workspace_bytes(ctypes.byref(dev.desc)))
+
+
+def df11_decode_gemv(dev: DeviceEncoded, mats: list[GemvMatrix], x, y, workspace,
+                     stream=None) -> None:
+    """Enqueue y = W x for every matrix of ``dev`` (x a bfloat16 and y a float32
+    CUDA tensor, workspace a CUDA tensor of at least df11_gemv_workspace_bytes
+    bytes)."""
+    import torch
+    if x.dtype != torch.bfloat16 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous bfloat16 tensor")
+    if y.dtype != torch.float32 or not y.is_contiguous():
+        raise ValueError("y must be a contiguous float32 tensor")
+    if stream is None:
+        stream = torch.cuda.current_stream(y.device)
+    arr = (GemvMatrix * len(mats))(*mats)
+    nbytes = workspace.numel() * workspace.element_size()
+    _check("df11_decode_gemv", _load().df11_decode_gemv(
+        ctypes.byref(dev.desc), arr, len(mats), x.data_ptr(), y.data_ptr(),
+        workspace.data_ptr(), nbytes, stream.cuda_stream))

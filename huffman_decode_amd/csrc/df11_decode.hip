@@ -92,11 +92,20 @@ static_assert(kTilesBytes < 0x10000, "tile addresses must fit 16 bits");
 #endif
 // sign|mantissa groups of 8 per lane loaded up front
 constexpr int kPrefetchGroups = DF11_PREFETCH_GROUPS;
+static_assert(kPrefetchGroups >= 1, "at least one group is prefetched");
 
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 typedef __attribute__((address_space(3))) uint16_t lds_u16;
 typedef __attribute__((address_space(3))) uint32_t lds_u32;
 typedef __attribute__((address_space(3))) uint64_t lds_u64;
+// global-memory views: pointers that reach device code inside a struct would
+// otherwise be accessed with FLAT instructions, which also count against the
+// LDS wait counter
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(1))) const uint16_t g_cu16;
+typedef __attribute__((address_space(1))) const u32x4 g_cu32x4;
+typedef __attribute__((address_space(1))) f32x4 g_f32x4;
 
 __device__ __forceinline__ uint32_t lds_offset(const void *p) {
     // low 32 bits of a flat address inside the LDS aperture are the LDS offset
@@ -394,11 +403,130 @@ __device__ __forceinline__ uint32_t join1(uint32_t e, uint32_t sm) {
 
 // at least 6 waves per SIMD: keeps the register budget at 80 VGPRs, the
 // most that still lets 3 workgroups of 8 waves share a CU
+// What a decoded block's BF16 words go to.  The kernel body calls
+// begin(p0, base, j_lo, j_hi) once a block's output range is known (its full
+// 8-word groups are j in [j_lo, j_hi), group j at output index base + 8 j;
+// this lane handles j = lane + 64 i), group(pos, e8, sm8, i) for each full
+// group starting at output index pos, with i its round for this lane (the
+// first two rounds told apart, later ones passed as 2), one() for the single
+// head/tail words, and end(block) after the block.
+struct StoreSink {  // plain decode: BF16 words to out[]
+    uint16_t *out;
+    __device__ __forceinline__ void begin(uint32_t, uint32_t, uint32_t, uint32_t) {}
+    __device__ __forceinline__ void group(uint32_t pos, uint2 e8, uint2 sm8, int) {
+        *reinterpret_cast<uint4 *>(out + pos) = join8(e8, sm8);
+    }
+    __device__ __forceinline__ void one(uint32_t pos, uint32_t e, uint32_t sm) {
+        out[pos] = (uint16_t)join1(e, sm);
+    }
+    __device__ __forceinline__ void end(uint32_t, uint32_t) {}
+};
+
+// Fused GEMV: y = W x for row-major matrices laid end to end in the decoded
+// output.  Every matrix row holds at least 2048 words, so one block's output
+// (at most 4096 words) touches at most three rows; a wave sums its products
+// per row and stores the three sums and the first row's index per block.
+// df11_gemv_reduce_kernel then adds those per row in block order, so the
+// result does not depend on scheduling.
+constexpr int kGemvMaxMats = 16;
+constexpr uint32_t kGemvMinCols = 2048;
+struct GemvArgs {
+    const uint16_t *x;      // all matrices' BF16 x vectors, matrix m's at x + xoff[m]
+    float *y;               // all matrices' results, matrix m's at y + yoff[m]
+    float4 *partials;       // per block: row sums of its first three rows, first row (bits)
+    uint32_t n_mats;
+    uint32_t off[kGemvMaxMats + 1];   // first output index of each matrix; off[n_mats] = n
+    uint32_t cols[kGemvMaxMats];
+    uint32_t row0[kGemvMaxMats + 1];  // running row count before each matrix
+    uint32_t xoff[kGemvMaxMats];
+    uint32_t yoff[kGemvMaxMats];
+};
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+    return v;
+}
+
+// The matrix table in LDS (copied from the kernel argument once per workgroup).
+struct GemvTable {
+    uint32_t off[kGemvMaxMats + 1];
+    uint32_t cols[kGemvMaxMats];
+    uint32_t row0[kGemvMaxMats + 1];
+    uint32_t xoff[kGemvMaxMats];
+};
+
+struct DotSink {
+    const GemvTable *tab;  // in LDS
+    const g_cu16 *x;       // BF16
+    g_f32x4 *partials;
+    uint32_t n_mats, lane;
+    uint32_t s1, s2;     // first output index of the block's second and third row
+    // x index - output index: d0 in the first row, + dd1 from the second,
+    // + dd2 from the third (selecting among three fields would become an
+    // indexed load and keep this object in scratch memory)
+    uint32_t d0, dd1, dd2;
+    uint32_t grow;       // global index of the block's first row
+    float acc0, acc1, acc2;
+    __device__ __forceinline__ void begin(uint32_t p0, uint32_t, uint32_t, uint32_t) {
+        uint32_t m = 0;
+        while (m + 1 < n_mats && p0 >= tab->off[m + 1]) ++m;
+        const uint32_t c0 = tab->cols[m];
+        const uint32_t r = (p0 - tab->off[m]) / c0;
+        const uint32_t s0 = tab->off[m] + r * c0;
+        grow = tab->row0[m] + r;
+        d0 = tab->xoff[m] - s0;
+        s1 = s0 + c0;
+        const uint32_t m1 = (m + 1 < n_mats && s1 >= tab->off[m + 1]) ? m + 1 : m;
+        const uint32_t d1 = tab->xoff[m1] - s1;
+        s2 = s1 + tab->cols[m1];
+        const uint32_t m2 = (m1 + 1 < n_mats && s2 >= tab->off[m1 + 1]) ? m1 + 1 : m1;
+        const uint32_t d2 = tab->xoff[m2] - s2;
+        dd1 = d1 - d0;
+        dd2 = d2 - d1;
+        acc0 = acc1 = acc2 = 0.0f;
+    }
+    __device__ __forceinline__ void add(uint32_t pos, float v) {
+        acc0 += pos < s1 ? v : 0.0f;
+        acc1 += pos >= s1 && pos < s2 ? v : 0.0f;
+        acc2 += pos >= s2 ? v : 0.0f;
+    }
+    // x index of output index pos; modular 32-bit arithmetic keeps it exact
+    __device__ __forceinline__ uint32_t xi(uint32_t pos) const {
+        return pos + d0 + (pos >= s1 ? dd1 : 0u) + (pos >= s2 ? dd2 : 0u);
+    }
+    __device__ __forceinline__ void group(uint32_t pos, uint2 e8, uint2 sm8, int) {
+        const uint4 w = join8(e8, sm8);
+        const u32x4 xv = *(const g_cu32x4 *)(x + xi(pos));  // 8 BF16 inputs
+        // BF16 x BF16 products are exact in fp32; the sum is rounded per step
+        float v = bf16_lo(w.x) * bf16_lo(xv.x);
+        v = fmaf(bf16_hi(w.x), bf16_hi(xv.x), v);
+        v = fmaf(bf16_lo(w.y), bf16_lo(xv.y), v);
+        v = fmaf(bf16_hi(w.y), bf16_hi(xv.y), v);
+        v = fmaf(bf16_lo(w.z), bf16_lo(xv.z), v);
+        v = fmaf(bf16_hi(w.z), bf16_hi(xv.z), v);
+        v = fmaf(bf16_lo(w.w), bf16_lo(xv.w), v);
+        v = fmaf(bf16_hi(w.w), bf16_hi(xv.w), v);
+        add(pos, v);
+    }
+    __device__ __forceinline__ void one(uint32_t pos, uint32_t e, uint32_t sm) {
+        add(pos, bf16_lo(join1(e, sm)) * bf16_lo(x[xi(pos)]));
+    }
+    __device__ __forceinline__ void end(uint32_t blk, uint32_t) {
+        const float t0 = wave_sum(acc0), t1 = wave_sum(acc1), t2 = wave_sum(acc2);
+        if (lane == 0) partials[blk] = f32x4{t0, t1, t2, __uint_as_float(grow)};
+    }
+};
+
 #ifndef DF11_WAVES_PER_EU
 #define DF11_WAVES_PER_EU 6
 #endif
 #define DF11_OCCUPANCY_HINT __attribute__((amdgpu_waves_per_eu(DF11_WAVES_PER_EU)))
-__global__ __launch_bounds__(kGroupThreads) DF11_OCCUPANCY_HINT void df11_decode_kernel(DecodeArgs a) {
+template <class Sink>
+__device__ __forceinline__ void decode_blocks(const DecodeArgs &a, Sink &sink) {
     // LDS: per-wave regions (staging slots, then the exponent tile) | decode
     // table in one static array (fixed offsets fold into the ds_read/ds_write
     // immediates, and the regions sit at the lowest addresses so that their
@@ -472,7 +600,7 @@ __global__ __launch_bounds__(kGroupThreads) DF11_OCCUPANCY_HINT void df11_decode
         npos = a.block_pos[b + (lane & 1)];
     }
     asm volatile("" ::"v"(nd0), "v"(nd1), "v"(nd2), "v"(ng0), "v"(ng1), "v"(npos));
-    uint32_t k = 0;
+    uint32_t k = 0, cur_blk = 0;
     while (b != 0xFFFFFFFFu) {
         // Rotate the wave's issue priority from block to block.  At equal
         // priority a SIMD issues the oldest wave first, so with fixed shares of
@@ -562,6 +690,7 @@ __global__ __launch_bounds__(kGroupThreads) DF11_OCCUPANCY_HINT void df11_decode
         {
             const uint32_t nnb = nb != 0xFFFFFFFFu ? wg_block(__builtin_amdgcn_readfirstlane(pend))
                                                    : 0xFFFFFFFFu;
+            cur_blk = b;
             b = nb;  // the rest of this iteration only uses p0, p1 and the lanes' data
             nb = nnb;
             ++k;
@@ -570,8 +699,13 @@ __global__ __launch_bounds__(kGroupThreads) DF11_OCCUPANCY_HINT void df11_decode
         // it and leave its output unwritten
         if (!sane || total != p1 - p0) {
             if (lane == 0 && a.status) atomicAdd(a.status, 1u);
+            if (sane) {  // leave a defined (empty) result for the block
+                sink.begin(p0, base, 0, 0);
+                sink.end(cur_blk, lane);
+            }
             continue;
         }
+        sink.begin(p0, base, one_pass ? full_lo : 0u, one_pass ? full_hi : 0u);
         const uint32_t at = (p0 - base) + excl;  // tile position of this lane's first symbol
         const uint32_t stop = lim ? lim : 0u;
         const uint32_t start = lim ? gap : 0u;
@@ -598,20 +732,20 @@ __global__ __launch_bounds__(kGroupThreads) DF11_OCCUPANCY_HINT void df11_decode
             wave_lds_sync();
         }
         if (one_pass) {
-            // ---- merge with sign|mantissa, 8 BF16 per lane per 16-byte store
+            // ---- merge with sign|mantissa, 8 BF16 per lane per group
 #pragma unroll
             for (int i = 0; i < kPrefetchGroups; ++i) {
                 const uint32_t j = lane + kWave * i;
                 if (j >= full_lo && j < full_hi)
-                    *reinterpret_cast<uint4 *>(a.out + base + 8 * j) =
-                        join8(*reinterpret_cast<const uint2 *>(tile + 8 * j), smv[i]);
+                    sink.group(base + 8 * j, *reinterpret_cast<const uint2 *>(tile + 8 * j), smv[i],
+                               i < 2 ? i : 2);
             }
             for (uint32_t j = lane + kWave * kPrefetchGroups; j < full_hi; j += kWave) {
                 const uint2 sm = *reinterpret_cast<const uint2 *>(a.signmant + base + 8 * j);
-                *reinterpret_cast<uint4 *>(a.out + base + 8 * j) =
-                    join8(*reinterpret_cast<const uint2 *>(tile + 8 * j), sm);
+                sink.group(base + 8 * j, *reinterpret_cast<const uint2 *>(tile + 8 * j), sm,
+                           kPrefetchGroups < 2 ? 2 : kPrefetchGroups);
             }
-            if (edge) a.out[edge_i] = (uint16_t)join1(tile[edge_i - base], edge_sm);
+            if (edge) sink.one(edge_i, tile[edge_i - base], edge_sm);
             wave_lds_sync();
         } else {
             // more symbols than one tile holds: decode again per tile-sized window
@@ -623,29 +757,86 @@ __global__ __launch_bounds__(kGroupThreads) DF11_OCCUPANCY_HINT void df11_decode
                 for (uint32_t j = r0 / 8 + lane; j < j_hi; j += kWave) {
                     if (j < full_lo || j >= full_hi) continue;  // edge groups: below
                     const uint2 sm = *reinterpret_cast<const uint2 *>(a.signmant + base + 8 * j);
-                    *reinterpret_cast<uint4 *>(a.out + base + 8 * j) =
-                        join8(*reinterpret_cast<const uint2 *>(tile + 8 * j - r0), sm);
+                    sink.group(base + 8 * j, *reinterpret_cast<const uint2 *>(tile + 8 * j - r0), sm, 2);
                 }
                 const uint32_t er = edge_i - base - r0;
-                if (edge && er < (uint32_t)kTileCap)
-                    a.out[edge_i] = (uint16_t)join1(tile[er], edge_sm);
+                if (edge && er < (uint32_t)kTileCap) sink.one(edge_i, tile[er], edge_sm);
                 wave_lds_sync();
             }
         }
+        sink.end(cur_blk, lane);
     }
 }
 
-// Launch shape per device: compute units and resident workgroups per CU for
-// each table count (the LDS footprint depends on it).
+__global__ __launch_bounds__(kGroupThreads) DF11_OCCUPANCY_HINT void df11_decode_kernel(DecodeArgs a) {
+    StoreSink sink{a.out};
+    decode_blocks(a, sink);
+}
+
+__global__ __launch_bounds__(kGroupThreads) DF11_OCCUPANCY_HINT void df11_gemv_kernel(DecodeArgs a,
+                                                                                    GemvArgs g) {
+    // the matrix table goes to LDS with constant indices (indexing the kernel
+    // argument at run time would make the compiler copy it to scratch); the
+    // first barrier in decode_blocks publishes it
+    __shared__ GemvTable tab;
+    if (threadIdx.x == 0) {
+#pragma unroll
+        for (int i = 0; i <= kGemvMaxMats; ++i) {
+            tab.off[i] = g.off[i];
+            tab.row0[i] = g.row0[i];
+        }
+#pragma unroll
+        for (int i = 0; i < kGemvMaxMats; ++i) {
+            tab.cols[i] = g.cols[i];
+            tab.xoff[i] = g.xoff[i];
+        }
+    }
+    DotSink sink;
+    sink.tab = &tab;
+    sink.x = (const g_cu16 *)g.x;
+    sink.partials = (g_f32x4 *)g.partials;
+    sink.n_mats = g.n_mats;
+    sink.lane = threadIdx.x % kWave;
+    decode_blocks(a, sink);
+}
+
+// y of every row: the sums its blocks stored, in block order.
+__global__ __launch_bounds__(256) void df11_gemv_reduce_kernel(GemvArgs g, const uint32_t *block_pos,
+                                                               uint32_t n_blocks) {
+    const uint32_t row = blockIdx.x * 256 + threadIdx.x;
+    if (row >= g.row0[g.n_mats]) return;
+    uint32_t m = 0;
+    while (m + 1 < g.n_mats && row >= g.row0[m + 1]) ++m;
+    const uint32_t r = row - g.row0[m];
+    const uint32_t rs = g.off[m] + r * g.cols[m], re = rs + g.cols[m];
+    // the last block starting at or before rs: block_pos[lo] <= rs < block_pos[hi]
+    uint32_t lo = 0, hi = n_blocks;
+    while (hi - lo > 1) {
+        const uint32_t mid = (lo + hi) / 2;
+        if (block_pos[mid] <= rs) lo = mid; else hi = mid;
+    }
+    float sum = 0.0f;
+    for (uint32_t b = lo; b < n_blocks && block_pos[b] < re; ++b) {
+        const float4 p = g.partials[b];
+        const uint32_t seg = row - __float_as_uint(p.w);
+        sum += seg == 0 ? p.x : (seg == 1 ? p.y : (seg == 2 ? p.z : 0.0f));
+    }
+    g.y[g.yoff[m] + r] = sum;
+}
+
+// Launch shape per device: compute units and, per kernel, resident
+// workgroups per CU for each table count (the LDS footprint depends on it).
 constexpr int kMaxDevices = 16;
+constexpr int kKernels = 2;  // 0: decode, 1: fused GEMV
 std::atomic<int> g_cus[kMaxDevices];
-std::atomic<int> g_occ[kMaxDevices][DF11_MAX_TABLES + 1];
+std::atomic<int> g_occ[kKernels][kMaxDevices][DF11_MAX_TABLES + 1];
 
 // dynamic LDS per workgroup: the 8-bit tables (tiles and fast tables are static)
 size_t lds_bytes(uint32_t n_tables) { return (size_t)n_tables * kTableBytes; }
 
-int launch_groups(int dev, uint32_t n_tables, uint32_t n_blocks, uint32_t max_groups,
-                  int *groups) {
+template <class K>
+int launch_groups(K kernel, int which, int dev, uint32_t n_tables, uint32_t n_blocks,
+                  uint32_t max_groups, int *groups) {
     if (dev < 0 || dev >= kMaxDevices) return DF11_ERR_HIP;
     int cus = g_cus[dev].load(std::memory_order_relaxed);
     if (cus <= 0) {
@@ -653,7 +844,7 @@ int launch_groups(int dev, uint32_t n_tables, uint32_t n_blocks, uint32_t max_gr
             return DF11_ERR_HIP;
         g_cus[dev].store(cus, std::memory_order_relaxed);
     }
-    int occ = g_occ[dev][n_tables].load(std::memory_order_relaxed);
+    int occ = g_occ[which][dev][n_tables].load(std::memory_order_relaxed);
     if (occ <= 0) {
         // a workgroup whose LDS exceeds what one CU can give it would never be
         // dispatched: refuse the launch instead
@@ -661,18 +852,17 @@ int launch_groups(int dev, uint32_t n_tables, uint32_t n_blocks, uint32_t max_gr
         hipFuncAttributes attr;
         if (hipDeviceGetAttribute(&max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) !=
                 hipSuccess ||
-            hipFuncGetAttributes(&attr, reinterpret_cast<const void *>(df11_decode_kernel)) !=
-                hipSuccess)
+            hipFuncGetAttributes(&attr, reinterpret_cast<const void *>(kernel)) != hipSuccess)
             return DF11_ERR_HIP;
         if (attr.sharedSizeBytes + lds_bytes(n_tables) > (size_t)max_lds) return DF11_ERR_TABLES;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, df11_decode_kernel, kGroupThreads,
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, kGroupThreads,
                                                          lds_bytes(n_tables)) != hipSuccess)
             return DF11_ERR_HIP;
         if (occ <= 0) return DF11_ERR_TABLES;
 #ifdef DF11_MAX_OCCUPANCY
         occ = occ < DF11_MAX_OCCUPANCY ? occ : DF11_MAX_OCCUPANCY;
 #endif
-        g_occ[dev][n_tables].store(occ, std::memory_order_relaxed);
+        g_occ[which][dev][n_tables].store(occ, std::memory_order_relaxed);
     }
     // a multiple of the XCD count, no more than there are blocks to share
     const uint64_t want = ((uint64_t)n_blocks + kWavesPerGroup - 1) / kWavesPerGroup;
@@ -689,10 +879,9 @@ int launch_groups(int dev, uint32_t n_tables, uint32_t n_blocks, uint32_t max_gr
 
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-}  // namespace
-
-extern "C" int df11_decode(const df11_device_stream *s, uint16_t *out, void *hip_stream) {
-    if (!s || !out || !s->stream || !s->gaps || !s->block_pos || !s->signmant || !s->luts)
+// Checks a descriptor and fills the kernel arguments (out may be null).
+int prepare(const df11_device_stream *s, uint16_t *out, DecodeArgs *a) {
+    if (!s || !s->stream || !s->gaps || !s->block_pos || !s->signmant || !s->luts)
         return DF11_ERR_ARG;
     if (s->n == 0 || s->n > DF11_MAX_N) return DF11_ERR_ARG;
     if (!aligned(out, 16) || !aligned(s->stream, 8) || !aligned(s->signmant, 8) ||
@@ -710,29 +899,89 @@ extern "C" int df11_decode(const df11_device_stream *s, uint16_t *out, void *hip
         s->signmant_bytes < ((s->n + 7) & ~uint64_t(7)) ||
         s->lut_bytes < df11_internal::lut_image_bytes(s->n_tables))
         return DF11_ERR_BUFSIZE;
+    a->stream = reinterpret_cast<const uint32_t *>(s->stream);
+    a->gaps = reinterpret_cast<const uint32_t *>(s->gaps);
+    a->block_pos = s->block_pos;
+    a->signmant = s->signmant;
+    a->luts = reinterpret_cast<const uint4 *>(s->luts);
+    a->out = out;
+    a->status = s->status;
+    a->n = s->n;
+    a->total_bits = s->total_bits;
+    a->stop_bit = s->last_start + 1;
+    a->n_blocks = s->n_blocks;
+    a->n_tables = s->n_tables;
+    a->max_len = s->max_len;
+    a->blocks_per_xcd = (s->n_blocks + kXcds - 1) / kXcds;
+    return DF11_OK;
+}
 
+}  // namespace
+
+extern "C" int df11_decode(const df11_device_stream *s, uint16_t *out, void *hip_stream) {
+    if (!out) return DF11_ERR_ARG;
+    DecodeArgs a;
+    int st = prepare(s, out, &a);
+    if (st != DF11_OK) return st;
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return DF11_ERR_HIP;
     int groups = 0;
-    int st = launch_groups(dev, s->n_tables, s->n_blocks, s->max_groups, &groups);
+    st = launch_groups(df11_decode_kernel, 0, dev, s->n_tables, s->n_blocks, s->max_groups, &groups);
     if (st != DF11_OK) return st;
-
-    DecodeArgs a;
-    a.stream = reinterpret_cast<const uint32_t *>(s->stream);
-    a.gaps = reinterpret_cast<const uint32_t *>(s->gaps);
-    a.block_pos = s->block_pos;
-    a.signmant = s->signmant;
-    a.luts = reinterpret_cast<const uint4 *>(s->luts);
-    a.out = out;
-    a.status = s->status;
-    a.n = s->n;
-    a.total_bits = s->total_bits;
-    a.stop_bit = s->last_start + 1;
-    a.n_blocks = s->n_blocks;
-    a.n_tables = s->n_tables;
-    a.max_len = s->max_len;
-    a.blocks_per_xcd = (s->n_blocks + kXcds - 1) / kXcds;
     hipLaunchKernelGGL(df11_decode_kernel, dim3(groups), dim3(kGroupThreads),
                        lds_bytes(s->n_tables), static_cast<hipStream_t>(hip_stream), a);
+    return hipGetLastError() == hipSuccess ? DF11_OK : DF11_ERR_HIP;
+}
+
+extern "C" uint64_t df11_gemv_workspace_bytes(const df11_device_stream *s) {
+    return s ? 16ull * s->n_blocks : 0;
+}
+
+extern "C" int df11_decode_gemv(const df11_device_stream *s, const df11_gemv_matrix *mats,
+                                uint32_t n_mats, const uint16_t *x, float *y, void *workspace,
+                                uint64_t workspace_bytes, void *hip_stream) {
+    if (!mats || !x || !y || !workspace) return DF11_ERR_ARG;
+    DecodeArgs a;
+    int st = prepare(s, nullptr, &a);
+    if (st != DF11_OK) return st;
+    if (n_mats < 1 || n_mats > (uint32_t)kGemvMaxMats || !aligned(x, 16) || !aligned(y, 4) ||
+        !aligned(workspace, 16))
+        return DF11_ERR_ARG;
+    if (workspace_bytes < df11_gemv_workspace_bytes(s)) return DF11_ERR_BUFSIZE;
+    GemvArgs g;
+    g.x = x;
+    g.y = y;
+    g.partials = static_cast<float4 *>(workspace);
+    g.n_mats = n_mats;
+    uint64_t off = 0, rows = 0;
+    for (uint32_t m = 0; m < n_mats; ++m) {
+        const df11_gemv_matrix &mm = mats[m];
+        // matrices end to end in output order; rows long enough that a block
+        // touches at most three of them; 8-aligned groups never straddle rows
+        if (mm.offset != off || mm.rows == 0 || mm.cols < kGemvMinCols || mm.cols % 8 != 0 ||
+            mm.x_offset % 8 != 0)
+            return DF11_ERR_ARG;
+        g.off[m] = (uint32_t)off;
+        g.cols[m] = mm.cols;
+        g.row0[m] = (uint32_t)rows;
+        g.xoff[m] = mm.x_offset;
+        g.yoff[m] = mm.y_offset;
+        off += (uint64_t)mm.rows * mm.cols;
+        rows += mm.rows;
+        if (off > s->n || rows >= 0x80000000ull) return DF11_ERR_ARG;
+    }
+    if (off != s->n) return DF11_ERR_ARG;
+    g.off[n_mats] = (uint32_t)off;
+    g.row0[n_mats] = (uint32_t)rows;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return DF11_ERR_HIP;
+    int groups = 0;
+    st = launch_groups(df11_gemv_kernel, 1, dev, s->n_tables, s->n_blocks, s->max_groups, &groups);
+    if (st != DF11_OK) return st;
+    const hipStream_t hs = static_cast<hipStream_t>(hip_stream);
+    hipLaunchKernelGGL(df11_gemv_kernel, dim3(groups), dim3(kGroupThreads), lds_bytes(s->n_tables),
+                       hs, a, g);
+    hipLaunchKernelGGL(df11_gemv_reduce_kernel, dim3((uint32_t)((rows + 255) / 256)), dim3(256), 0,
+                       hs, g, a.block_pos, a.n_blocks);
     return hipGetLastError() == hipSuccess ? DF11_OK : DF11_ERR_HIP;
 }

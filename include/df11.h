@@ -167,6 +167,40 @@ typedef struct df11_device_stream {
  * it never makes the kernel read or write outside the stated buffers. */
 int df11_decode(const df11_device_stream *s, uint16_t *out, void *hip_stream);
 
+/* ------------------------------------------------------------------ GEMV */
+
+/* One row-major [rows, cols] matrix of a decoded stream, for the fused GEMV. */
+typedef struct df11_gemv_matrix {
+    uint64_t offset;   /* index of its first weight in the decoded output */
+    uint32_t rows, cols;
+    uint32_t x_offset; /* its input is x[x_offset .. x_offset + cols); multiple of 8 */
+    uint32_t y_offset; /* its result goes to y[y_offset .. y_offset + rows) */
+} df11_gemv_matrix;
+
+#define DF11_GEMV_MAX_MATRICES 16
+#define DF11_GEMV_MIN_COLS 2048
+
+/* Bytes of device workspace df11_decode_gemv needs for s (16 per block). */
+uint64_t df11_gemv_workspace_bytes(const df11_device_stream *s);
+
+/* Fused decode and matrix-vector product: for each matrix m,
+ * y[y_offset_m + r] = sum_c W_m[r][c] * x[x_offset_m + c] (products of the
+ * decoded BF16 weights with the BF16 inputs, exact in fp32, summed in fp32),
+ * without writing the BF16 weights anywhere.  This is the decompress-then-matmul step of DF11
+ * inference (section "Architecture") at batch 1, with the decompressed block
+ * kept on chip.  The n_mats (1..16) matrices must lie end to end in output
+ * order from offset 0 and cover all n weights; cols must be a multiple of 8
+ * and at least 2048.  x is a device array of BF16 words (16-byte aligned), y
+ * a device fp32 array (4-byte aligned); workspace is caller-owned device memory of at least
+ * df11_gemv_workspace_bytes(s), 16-byte aligned, overwritten.  Each row's sum
+ * is formed in a fixed order (per block, then blocks in stream order), so the
+ * result is the same on every run.  Two kernels are enqueued on hip_stream.
+ * Errors: those of df11_decode, ARG for a matrix list that breaks the rules,
+ * BUFSIZE for a short workspace. */
+int df11_decode_gemv(const df11_device_stream *s, const df11_gemv_matrix *mats, uint32_t n_mats,
+                     const uint16_t *x, float *y, void *workspace, uint64_t workspace_bytes,
+                     void *hip_stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -152,3 +152,65 @@ def test_stack_pipeline_overlapped_matches_bf16_gemms(torch):
             for i in range(len(blocks)):
                 for sh in ref[i]:
                     assert torch.equal(outs[i][sh], ref[i][sh]), (mode, batch, i, sh)
+
+
+# ---------------------------------------------------------------------------
+# Fused decode + GEMV.  Reference: the plain product of the original BF16
+# weights with the BF16 x, both as float64, by numpy.  BF16 x BF16 products are
+# exact in fp32; the kernel forms each row's sum in fp32 with at most 8 (per
+# group) + 16 (groups per lane) + 6 (wave tree) + 16 (blocks per row, cols <=
+# 16384 over >= 1000 weights per block) = 46 rounded additions, so
+# |y - ref| <= 46 * 2^-24 * sum|w x| bounds the error; the test uses
+# 2^-18 * sum|w x| (64 * 2^-24).
+
+def _gemv_check(torch, w, shapes, label, seed=7):
+    enc = hd.encode(w)
+    dev = hd.to_device(enc)
+    mats, nx, ny = hd.gemv_matrices(shapes)
+    rng = np.random.default_rng(seed)
+    x_bits = wl.to_bf16(rng.standard_normal(nx).astype(np.float32))
+    x = torch.from_numpy(x_bits.view(np.int16)).cuda().view(torch.bfloat16)
+    x_host = torch.from_numpy(x_bits.view(np.int16)).view(torch.bfloat16).float().numpy()
+    ws = torch.empty(hd.df11_gemv_workspace_bytes(dev), dtype=torch.uint8, device="cuda")
+    ys = []
+    for fill in (1.0e30, -7.0):
+        y = torch.full((ny,), fill, dtype=torch.float32, device="cuda")
+        _say(f"[gpu] df11_decode_gemv {label} n={enc.n} mats={len(mats)} fill={fill}")
+        hd.df11_decode_gemv(dev, mats, x, y, ws)
+        torch.cuda.synchronize()
+        ys.append(y.cpu().numpy())
+    assert np.array_equal(ys[0].view(np.uint32), ys[1].view(np.uint32)), "not deterministic"
+    wf = torch.from_numpy(w.view(np.int16)).view(torch.bfloat16).float().numpy().astype(np.float64)
+    off = 0
+    for m, (r, c) in zip(mats, shapes):
+        W = wf[off: off + r * c].reshape(r, c)
+        xv = x_host[m.x_offset: m.x_offset + c].astype(np.float64)
+        ref = W @ xv
+        bound = np.abs(W) @ np.abs(xv) * 2.0 ** -18 + 1e-30
+        got = ys[0][m.y_offset: m.y_offset + r].astype(np.float64)
+        bad = np.abs(got - ref) > bound
+        assert not bad.any(), (label, m.rows, m.cols, int(bad.sum()))
+        off += r * c
+
+
+@pytest.mark.parametrize("name,make,scale", [
+    ("llama8b_1_64", lambda: wl.llama8b_block(seed=11, scale=1 / 64), None),
+    ("flux_1_64", lambda: wl.flux_block(12, scale=1 / 64), None),
+    ("ragged_rows", lambda: wl.normal_block("r", [("a", 37, 2048), ("b", 5, 6144), ("c", 129, 2056)],
+                                            13, 0.02), None),
+])
+def test_fused_gemv_small(torch, name, make, scale):
+    wlx = make()
+    _gemv_check(torch, wlx.weights, [(m.rows, m.cols) for m in wlx.matrices], name)
+
+
+def test_fused_gemv_single_exponent_fallback(torch):
+    """A one-exponent tensor has 1-bit codes: every block takes the re-decode
+    route and several tile passes."""
+    w = wl.random_small(64 * 4096, 21, "single")
+    _gemv_check(torch, w, [(64, 4096)], "single")
+
+
+def test_fused_gemv_llama8b_block(torch):
+    wlx = wl.llama8b_block()
+    _gemv_check(torch, wlx.weights, [(m.rows, m.cols) for m in wlx.matrices], "llama8b_block")

@@ -228,3 +228,40 @@ def _model_blocks(enc, blocks):
         smb = enc.signmant[p0:p1].astype(np.uint16)
         res[b] = ((smb & 0x80) << 8) | (ex << 7) | (smb & 0x7F)
     return res
+
+
+def test_decode_gemv_rejects_bad_matrix_lists_on_host():
+    """The fused GEMV checks its matrix list before any device call."""
+    lib = hd.library()
+    w = wl.random_small(3 * 4096 * 8, 5, "normal")
+    enc = hd.encode(w)
+    sz = enc.sizes
+    d = hd.DeviceStream()
+    fake = 1 << 20
+    d.stream = d.gaps = d.block_pos = d.signmant = d.luts = fake
+    d.stream_bytes, d.gaps_bytes = sz.stream_bytes, sz.gaps_bytes
+    d.block_pos_count, d.signmant_bytes, d.lut_bytes = sz.block_pos_count, sz.signmant_bytes, \
+        sz.lut_bytes
+    d.n, d.total_bits, d.last_start = sz.n, sz.total_bits, sz.last_start
+    d.n_blocks, d.n_tables, d.max_len = sz.n_blocks, enc.codebook.n_tables, enc.codebook.max_len
+    assert lib.df11_gemv_workspace_bytes(ctypes.byref(d)) == 16 * sz.n_blocks
+    ws = 16 * sz.n_blocks
+
+    def call(shapes, x=fake, wsb=ws, mats=None):
+        mats = mats if mats is not None else hd.gemv_matrices(shapes)[0]
+        arr = (hd.GemvMatrix * len(mats))(*mats)
+        return lib.df11_decode_gemv(ctypes.byref(d), arr, len(mats), x, fake, fake, wsb, None)
+
+    assert call([(24, 4096)], wsb=ws - 16) == -2          # workspace too small
+    assert call([(24, 4096)], x=fake + 4) == -1           # x not 16-byte aligned
+    assert call([(48, 2048), (1, 0)]) == -1                # empty matrix
+    assert call([(96, 1024)]) == -1                        # rows shorter than 2048
+    assert call([(23, 4096)]) == -1                        # does not cover all weights
+    assert call([(12, 4100), (12, 4092)]) == -1            # cols not a multiple of 8
+    mats, _, _ = hd.gemv_matrices([(12, 4096), (12, 4096)])
+    mats[1].offset += 8
+    assert call(None, mats=mats) == -1                     # gap between matrices
+    mats, _, _ = hd.gemv_matrices([(12, 4096), (12, 4096)])
+    mats[1].x_offset += 4
+    assert call(None, mats=mats) == -1                     # x slice not 8-aligned
+    assert call([(1, 4096)] * 17 + [(7, 4096)]) == -1      # more than 16 matrices
