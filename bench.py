@@ -276,6 +276,70 @@ def fused_gemv(wlx, copies, stream, reps=20) -> dict:
     return {"fused_ms": round(ms, 5)}
 
 
+def run_offload(args) -> int:
+    """CPU offload over the 8B-shaped stack: compressed blocks in pinned host
+    memory, each copied to the GPU and decoded in turn (copies overlapped with
+    the previous block's decode).  Reports the PCIe-inclusive time per block
+    next to the decode of device-resident blocks."""
+    import numpy as np
+    import torch
+    import huffman_decode_amd as hd
+    from huffman_decode_amd import workloads as wl
+    from huffman_decode_amd.pipeline import OffloadRunner
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    encs, origs = [], []
+    for layer in range(args.layers):
+        wlx = wl.llama8b_stack_block(layer)
+        encs.append(hd.encode(wlx.weights))
+        origs.append(wlx.weights[:: 997].copy())  # a sample to check against
+        print(f"[offload] layer {layer} encoded", file=sys.stderr, flush=True)
+    sums = [e.checksum() for e in encs]
+    runner = OffloadRunner(encs, sums, dev)
+    exact = True
+
+    def check(i, out):
+        nonlocal exact
+        got = out[:: 997].view(torch.int16).cpu().numpy().view(np.uint16)
+        exact &= bool(np.array_equal(got, origs[i]))
+
+    runner.run(check)
+    torch.cuda.synchronize()
+    cs = runner.compute_stream
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    runner.run()
+    torch.cuda.synchronize()
+    e0.record(cs)
+    for _ in range(args.steps):
+        runner.run()
+    e1.record(cs)
+    torch.cuda.synchronize()
+    t_off = e0.elapsed_time(e1) / args.steps
+    # the same blocks resident in device memory
+    resident = [hd.to_device(e, dev) for e in encs]
+    buf = runner.buffers[0]
+    for d in resident:
+        hd.df11_decode(d, buf)
+    torch.cuda.synchronize()
+    e0.record(cs)
+    for _ in range(args.steps):
+        for d in resident:
+            hd.df11_decode(d, buf)
+    e1.record(cs)
+    torch.cuda.synchronize()
+    t_res = e0.elapsed_time(e1) / args.steps
+    comp = sum(e.compressed_bytes() for e in encs)
+    n = sum(e.n for e in encs)
+    print(json.dumps({"mode": "offload", "workload": "llama8b_stack", "layers": args.layers,
+                      "n_weights": n, "compressed_bytes": comp, "bit_exact_sampled": exact,
+                      "offload_ms_per_block": round(t_off / args.layers, 4),
+                      "resident_ms_per_block": round(t_res / args.layers, 4),
+                      "host_to_device_GBps": round(comp / (t_off * 1e-3) / 1e9, 2),
+                      "offload_over_resident": round(t_off / t_res, 3)}), flush=True)
+    return 0 if exact else 1
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -286,10 +350,12 @@ def main() -> int:
                     help="rotating encoded copies (defeats the Infinity Cache)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-gemm", action="store_true", help="skip the decode/GEMM ratios")
-    ap.add_argument("--mode", choices=("decode", "copy", "stack", "encode"), default="decode",
+    ap.add_argument("--mode", choices=("decode", "copy", "stack", "encode", "offload"),
+                    default="decode",
                     help="copy: time a plain device copy of --copy-mib MiB instead; "
                          "stack: decode/GEMM schedules over the 32-block 8B-shaped stack; "
-                         "encode: host encoder throughput (no GPU)")
+                         "encode: host encoder throughput (no GPU); "
+                         "offload: blocks from pinned host memory, copied and decoded in turn")
     ap.add_argument("--layers", type=int, default=32, help="blocks in the stack mode")
     ap.add_argument("--copy-mib", type=int, default=1024)
     args = ap.parse_args()
@@ -306,6 +372,8 @@ def main() -> int:
         return run_stack(args)
     if args.mode == "encode":
         return run_encode(args)
+    if args.mode == "offload":
+        return run_offload(args)
 
     import numpy as np
     import torch

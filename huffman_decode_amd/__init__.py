@@ -178,6 +178,18 @@ class Encoded:
         return int(s.stream_bytes + s.gaps_bytes + 4 * s.block_pos_count + s.signmant_bytes
                    + s.lut_bytes)
 
+    def checksum(self) -> int:
+        """CRC-32 (zlib's) over the arrays the decoder reads, in the order
+        stream, gaps, block_pos, sign|mantissa, tables.  The code stream is
+        not self-synchronising (one flipped bit corrupts the rest of its
+        block), so a stored artifact carries this value and is checked
+        against it when loaded."""
+        import zlib
+        c = 0
+        for arr in (self.stream, self.gaps, self.block_pos, self.signmant, self.luts):
+            c = zlib.crc32(np.ascontiguousarray(arr).view(np.uint8), c)
+        return c
+
 
 def df11_encode(bf16: np.ndarray, cb: Codebook, hist: np.ndarray | None = None,
                 n_threads: int = 0) -> Encoded:

@@ -128,3 +128,95 @@ class StackRunner:
         s = self.compute_stream
         for i, blk in enumerate(self.blocks):
             df11_decode(blk.dev, self.buffers[i % 2], s)
+
+
+class OffloadRunner:
+    """CPU offload: the encoded blocks stay in pinned host memory and each is
+    copied to the GPU just before its decode (the DF11 pages' offload mode,
+    which trades PCIe traffic for GPU memory).  Two device staging slots
+    alternate: block i+1's arrays are copied on a copy stream while block i
+    decodes.  Device memory holds two blocks' compressed arrays and two BF16
+    buffers.  Every block's checksum is verified when it is placed in host
+    memory."""
+
+    _ARRAYS = ("stream", "gaps", "block_pos", "signmant", "luts")
+
+    def __init__(self, encoded: list, checksums: list[int], device="cuda"):
+        import numpy as np
+        import torch
+        from . import _descriptor, to_device
+        if len(encoded) != len(checksums) or not encoded:
+            raise ValueError("one checksum per encoded block")
+        for i, (enc, want) in enumerate(zip(encoded, checksums)):
+            got = enc.checksum()
+            if got != want:
+                raise ValueError(f"block {i}: checksum mismatch: stored {want:#010x}, "
+                                 f"data {got:#010x}")
+        self.device = torch.device(device)
+        self.encoded = encoded
+        self.host = []
+        for enc in encoded:
+            pinned = {}
+            for name in self._ARRAYS:
+                arr = getattr(enc, name)
+                if name == "block_pos":
+                    arr = arr.view(np.int32)
+                t = torch.empty(arr.shape, dtype=torch.from_numpy(arr[:0]).dtype, pin_memory=True)
+                t.copy_(torch.from_numpy(arr))
+                pinned[name] = t
+            self.host.append(pinned)
+        # staging slots sized for the largest block
+        self.slots = []
+        for _ in range(2):
+            t = {name: torch.empty(max(h[name].numel() for h in self.host),
+                                   dtype=self.host[0][name].dtype, device=self.device)
+                 for name in self._ARRAYS}
+            self.slots.append(t)
+        self._descriptor = _descriptor
+        n_max = max(e.n for e in encoded)
+        self.buffers = [torch.empty(n_max, dtype=torch.bfloat16, device=self.device)
+                        for _ in range(2)]
+        self.copy_stream = torch.cuda.Stream(device=self.device)
+        self.compute_stream = torch.cuda.current_stream(self.device)
+
+    def _desc(self, i, slot):
+        enc = self.encoded[i]
+        views = {name: self.slots[slot][name][: self.host[i][name].numel()]
+                 for name in self._ARRAYS}
+        return self._descriptor(enc.sizes, enc.codebook, views)
+
+    def run(self, consume=None):
+        """Copy and decode every block in order; consume(i, bf16) (optional)
+        is enqueued on the compute stream after block i's decode.  Returns the
+        BF16 buffer of the last block."""
+        import torch
+        from . import df11_decode, DeviceEncoded
+        cs, xs = self.compute_stream, self.copy_stream
+        n = len(self.encoded)
+        copied = [torch.cuda.Event() for _ in range(n)]
+        used = [torch.cuda.Event() for _ in range(n)]
+        xs.wait_stream(cs)
+
+        def copy(i):
+            slot = i % 2
+            if i >= 2:
+                xs.wait_event(used[i - 2])  # slot i % 2 was block i-2's
+            with torch.cuda.stream(xs):
+                for name in self._ARRAYS:
+                    src = self.host[i][name]
+                    self.slots[slot][name][: src.numel()].copy_(src, non_blocking=True)
+            copied[i].record(xs)
+
+        copy(0)
+        for i in range(n):
+            if i + 1 < n:
+                copy(i + 1)
+            cs.wait_event(copied[i])
+            dev = DeviceEncoded(self._desc(i, i % 2), self.slots[i % 2], self.encoded[i].n)
+            out = self.buffers[i % 2]
+            df11_decode(dev, out, cs)
+            if consume is not None:
+                consume(i, out[: self.encoded[i].n])
+            used[i].record(cs)
+        cs.wait_stream(xs)
+        return self.buffers[(n - 1) % 2][: self.encoded[-1].n]

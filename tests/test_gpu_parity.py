@@ -214,3 +214,22 @@ def test_fused_gemv_single_exponent_fallback(torch):
 def test_fused_gemv_llama8b_block(torch):
     wlx = wl.llama8b_block()
     _gemv_check(torch, wlx.weights, [(m.rows, m.cols) for m in wlx.matrices], "llama8b_block")
+
+
+def test_offload_runner_decodes_blocks_from_pinned_host_memory(torch):
+    """CPU offload: blocks copied from pinned host memory per decode, two
+    staging slots reused in turn; every block bit-exact."""
+    from huffman_decode_amd.pipeline import OffloadRunner
+    ws = [wl.llama8b_block(seed=(3001, layer), scale=1 / 64).weights for layer in range(5)]
+    encs = [hd.encode(w) for w in ws]
+    runner = OffloadRunner(encs, [e.checksum() for e in encs])
+    seen = {}
+
+    def keep(i, out):
+        seen[i] = out.view(torch.int16).clone()
+
+    _say("[gpu] offload runner, 5 blocks")
+    runner.run(keep)
+    torch.cuda.synchronize()
+    for i, w in enumerate(ws):
+        assert np.array_equal(seen[i].cpu().numpy().view(np.uint16), w), i

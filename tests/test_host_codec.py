@@ -265,3 +265,23 @@ def test_decode_gemv_rejects_bad_matrix_lists_on_host():
     mats[1].x_offset += 4
     assert call(None, mats=mats) == -1                     # x slice not 8-aligned
     assert call([(1, 4096)] * 17 + [(7, 4096)]) == -1      # more than 16 matrices
+
+
+def test_checksum_detects_a_flipped_bit_and_offload_refuses_it():
+    """One flipped stream bit desynchronises the decoder (the pages' failure
+    mode), so artifacts carry a CRC-32 of their arrays; the offload runner
+    checks it before using a block."""
+    from huffman_decode_amd.pipeline import OffloadRunner
+    enc = hd.encode(wl.random_small(50_000, 17, "normal"))
+    good = enc.checksum()
+    assert good == enc.checksum()
+    for name in ("stream", "gaps", "block_pos", "signmant", "luts"):
+        arr = getattr(enc, name)
+        b = arr.view(np.uint8)
+        b[b.size // 3] ^= 0x10
+        assert enc.checksum() != good, name
+        b[b.size // 3] ^= 0x10
+    assert enc.checksum() == good
+    enc.stream[100] ^= 1
+    with pytest.raises(ValueError, match="checksum mismatch"):
+        OffloadRunner([enc], [good])
