@@ -126,7 +126,7 @@ struct DecodeArgs {
     uint32_t n_blocks;
     uint32_t n_tables;
     uint32_t max_len;
-    uint32_t blocks_per_xcd;  // contiguous block range of one XCD
+    uint32_t range_start[kXcds + 1];  // first block of each XCD's range, then n_blocks
 };
 
 // 8-bit table entry: leaf = symbol | (length - 1) << 8; pointer = 0x8000 |
@@ -564,9 +564,16 @@ __device__ __forceinline__ void decode_blocks(const DecodeArgs &a, Sink &sink) {
     const uint32_t xcd = blockIdx.x % kXcds;
     const uint32_t slot = blockIdx.x / kXcds;
     const uint32_t groups_per_xcd = gridDim.x / kXcds;
-    const uint32_t range_lo = xcd * a.blocks_per_xcd;
-    uint32_t range_hi = range_lo + a.blocks_per_xcd;
-    range_hi = range_hi < a.n_blocks ? range_hi : a.n_blocks;
+    // (a switch with constant indices: indexing the kernel argument at run
+    // time would make the compiler copy it to scratch memory)
+    uint32_t range_lo = 0, range_hi = 0;
+    switch (xcd) {
+#define DF11_RANGE_CASE(x) \
+    case x: range_lo = a.range_start[x]; range_hi = a.range_start[x + 1]; break;
+        DF11_RANGE_CASE(0) DF11_RANGE_CASE(1) DF11_RANGE_CASE(2) DF11_RANGE_CASE(3)
+        DF11_RANGE_CASE(4) DF11_RANGE_CASE(5) DF11_RANGE_CASE(6) DF11_RANGE_CASE(7)
+#undef DF11_RANGE_CASE
+    }
     const uint32_t stride = groups_per_xcd * kWavesPerGroup;
 
     // slice g = 64 b + lane: its stream dwords are 2g..2g+2 and its 5-bit
@@ -912,7 +919,21 @@ int prepare(const df11_device_stream *s, uint16_t *out, DecodeArgs *a) {
     a->n_blocks = s->n_blocks;
     a->n_tables = s->n_tables;
     a->max_len = s->max_len;
-    a->blocks_per_xcd = (s->n_blocks + kXcds - 1) / kXcds;
+    // the caller's balanced ranges, or equal numbers of blocks
+    static_assert(DF11_RANGES == kXcds, "one block range per XCD");
+    if (s->range_start[kXcds] == 0) {
+        const uint32_t per = (s->n_blocks + kXcds - 1) / kXcds;
+        for (int r = 0; r <= kXcds; ++r) {
+            const uint64_t v = (uint64_t)per * r;
+            a->range_start[r] = (uint32_t)(v < s->n_blocks ? v : s->n_blocks);
+        }
+    } else {
+        if (s->range_start[0] != 0 || s->range_start[kXcds] != s->n_blocks) return DF11_ERR_FORMAT;
+        for (int r = 0; r <= kXcds; ++r) {
+            if (r && s->range_start[r] < s->range_start[r - 1]) return DF11_ERR_FORMAT;
+            a->range_start[r] = s->range_start[r];
+        }
+    }
     return DF11_OK;
 }
 
