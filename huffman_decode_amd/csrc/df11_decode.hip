@@ -198,6 +198,14 @@ __device__ __forceinline__ uint32_t wave_inclusive_sum(uint32_t v) {
     return v;
 }
 
+// Workgroup barrier that orders LDS accesses only: global loads in flight
+// stay in flight across it (__syncthreads would wait for them).
+__device__ __forceinline__ void group_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -534,7 +542,7 @@ __device__ __forceinline__ void decode_blocks(const DecodeArgs &a, Sink &sink) {
     // tables in dynamic LDS.
     __shared__ __attribute__((aligned(16))) uint8_t lds_static[kStaticLds];
     __shared__ uint32_t wg_next;  // next block index of this workgroup's share
-    if (threadIdx.x == 0) wg_next = 0;
+    if (threadIdx.x == 0) wg_next = kWavesPerGroup;  // claims 0..7: one per wave, below
     uint8_t *tiles = lds_static;
     uint2 *dec_t = reinterpret_cast<uint2 *>(lds_static + kTilesBytes);
     extern __shared__ uint4 smem_u4[];
@@ -545,12 +553,6 @@ __device__ __forceinline__ void decode_blocks(const DecodeArgs &a, Sink &sink) {
         if (threadIdx.x == 0 && a.status) atomicAdd(a.status, 1u);
         return;
     }
-
-    uint4 *lut_u4 = reinterpret_cast<uint4 *>(lut);
-    for (uint32_t i = threadIdx.x; i < hier_bytes / 16; i += kGroupThreads) lut_u4[i] = a.luts[i];
-    __syncthreads();
-    build_decode_table(lut, dec_t, a.n_tables, a.max_len);
-    __syncthreads();
 
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const uint32_t lane = threadIdx.x % kWave;
@@ -596,16 +598,40 @@ __device__ __forceinline__ void decode_blocks(const DecodeArgs &a, Sink &sink) {
         if (lane == 0) v = atomicAdd(&wg_next, 1u);
         return v;
     };
-    uint32_t b = wg_block(__builtin_amdgcn_readfirstlane(claim()));
-    uint32_t nb = b != 0xFFFFFFFFu ? wg_block(__builtin_amdgcn_readfirstlane(claim())) : 0xFFFFFFFFu;
-    uint32_t nd0 = 0, nd1 = 0, nd2 = 0, ng0 = 0, ng1 = 0, npos = 0;
-    if (b != 0xFFFFFFFFu) {
-        const uint32_t *sp = stream_at(b);
+    // The 8-bit tables' load goes first (up to 16 tables, one 16-B load per
+    // thread; more tables are loaded below), then each wave's first block:
+    // wave w takes the workgroup's claim w without the counter, so that its
+    // loads are in flight while the tables are staged and the decode table is
+    // built.
+    const uint32_t lut_u4_count = hier_bytes / 16;
+    const bool lut_one_load = lut_u4_count <= kGroupThreads;
+    uint4 lv = {0, 0, 0, 0};
+    if (lut_one_load && threadIdx.x < lut_u4_count) lv = a.luts[threadIdx.x];
+    uint32_t b = wg_block(wave);
+    uint32_t nd0, nd1, nd2, ng0, ng1, npos;
+    {
+        // (a wave without blocks loads block 0's inputs and ignores them:
+        // unconditional loads let the staging below wait for the table load
+        // alone)
+        const uint32_t b0 = b != 0xFFFFFFFFu ? b : 0;
+        const uint32_t *sp = stream_at(b0);
         nd0 = sp[0], nd1 = sp[1], nd2 = sp[2];
-        const uint32_t *gp = gaps_at(b);
+        const uint32_t *gp = gaps_at(b0);
         ng0 = gp[0], ng1 = gp[1];
-        npos = a.block_pos[b + (lane & 1)];
+        npos = a.block_pos[b0 + (lane & 1)];
     }
+
+    uint4 *lut_u4 = reinterpret_cast<uint4 *>(lut);
+    if (lut_one_load) {
+        if (threadIdx.x < lut_u4_count) lut_u4[threadIdx.x] = lv;
+    } else {
+        for (uint32_t i = threadIdx.x; i < lut_u4_count; i += kGroupThreads) lut_u4[i] = a.luts[i];
+    }
+    group_lds_sync();
+    build_decode_table(lut, dec_t, a.n_tables, a.max_len);
+    group_lds_sync();
+
+    uint32_t nb = b != 0xFFFFFFFFu ? wg_block(__builtin_amdgcn_readfirstlane(claim())) : 0xFFFFFFFFu;
     asm volatile("" ::"v"(nd0), "v"(nd1), "v"(nd2), "v"(ng0), "v"(ng1), "v"(npos));
     uint32_t k = 0, cur_blk = 0;
     while (b != 0xFFFFFFFFu) {
