@@ -98,14 +98,13 @@ def run_copy(args) -> int:
     for _ in range(args.warmup):
         dst.copy_(src)
     torch.cuda.synchronize()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    t_begin, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_begin.record(stream)
     for k in range(args.steps):
-        starts[k].record(stream)
         dst.copy_(src)
-        ends[k].record(stream)
+    t_end.record(stream)
     torch.cuda.synchronize()
-    ms = sum(s.elapsed_time(e) for s, e in zip(starts, ends)) / args.steps
+    ms = t_begin.elapsed_time(t_end) / args.steps
     print(json.dumps({"mode": "copy", "bytes_read": nbytes, "bytes_written": nbytes,
                       "kernel_ms": round(ms, 5),
                       "GBps_read_plus_write": round(2 * nbytes / (ms * 1e-3) / 1e9, 1),
@@ -343,8 +342,10 @@ def run_offload(args) -> int:
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default 100 for decode and copy, else 20)")
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed steps first (default 10 for decode and copy, else 3)")
     ap.add_argument("--workload", default="llama8b_block")
     ap.add_argument("--copies", type=int, default=3,
                     help="rotating encoded copies (defeats the Infinity Cache)")
@@ -359,6 +360,11 @@ def main() -> int:
     ap.add_argument("--layers", type=int, default=32, help="blocks in the stack mode")
     ap.add_argument("--copy-mib", type=int, default=1024)
     args = ap.parse_args()
+    fast = args.mode in ("decode", "copy")
+    if args.steps is None:
+        args.steps = 100 if fast else 20
+    if args.warmup is None:
+        args.warmup = 10 if fast else 3
 
     if args.gpus != 1:
         print(json.dumps({"error": "df11_decode is measured on one GPU only (--gpus 1); "
@@ -399,6 +405,10 @@ def main() -> int:
         hd.df11_decode(copies[k % len(copies)], out, stream)
     torch.cuda.synchronize()
 
+    # Timed region: K launches back to back, each between a pair of events on
+    # the launch stream.  Whole-job time per step = first start to last end
+    # over K (gaps between launches included); the kernel's own launch
+    # duration = the mean of the K pairs.
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     torch.cuda.synchronize()
@@ -409,11 +419,12 @@ def main() -> int:
         ends[k].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-
     ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
-    avg_ms = sum(ms) / len(ms)
+    launch_ms = sum(ms) / len(ms)
+    avg_ms = starts[0].elapsed_time(ends[-1]) / args.steps
     rd, wr = algorithmic_bytes(enc)
     gbs = (rd + wr) / (avg_ms * 1e-3) / 1e9
+    kernel_gbs = (rd + wr) / (launch_ms * 1e-3) / 1e9
     orig = torch.from_numpy(wlx.weights.view(np.int16)).to(dev)
     bit_exact = bool(torch.equal(out.view(torch.int16), orig))
     traffic = measured_traffic(rd + wr)
@@ -433,8 +444,9 @@ def main() -> int:
         "data": "synthetic",
         "gweights_per_s": round(n / (avg_ms * 1e-3) / 1e9, 2),
         "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
-        "kernel_ms": {"mean": round(avg_ms, 5), "min": round(min(ms), 5),
-                      "median": round(sorted(ms)[len(ms) // 2], 5)},
+        "kernel_ms": {"whole_job_per_step": round(avg_ms, 5), "launch_mean": round(launch_ms, 5),
+                      "launch_min": round(min(ms), 5),
+                      "launch_median": round(sorted(ms)[len(ms) // 2], 5)},
         "bit_exact": bit_exact,
         "config": {"workload": args.workload, "n_weights": n,
                    "matrices": [f"{m.name}:{m.rows}x{m.cols}" for m in wlx.matrices],
@@ -443,8 +455,8 @@ def main() -> int:
                    "max_code_len": int(enc.codebook.max_len),
                    "n_tables": int(enc.codebook.n_tables),
                    "rotating_copies": len(copies), "host_encode_s": round(t_enc, 2)},
-        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+        "roofline": {"bound": "hbm", "achieved": round(kernel_gbs, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(kernel_gbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
                      "bytes_per_launch": {"read": rd, "written": wr}},
     }
