@@ -62,8 +62,7 @@ class DeviceStream(ctypes.Structure):
                 ("stream_bytes", _U64), ("gaps_bytes", _U64), ("block_pos_count", _U64),
                 ("signmant_bytes", _U64), ("lut_bytes", _U64), ("n", _U64),
                 ("total_bits", _U64), ("last_start", _U64), ("n_blocks", _U32),
-                ("n_tables", _U32), ("max_len", _U32), ("max_groups", _U32), ("status", _P),
-                ("range_start", _U32 * 9)]
+                ("n_tables", _U32), ("max_len", _U32), ("max_groups", _U32), ("status", _P)]
 
 
 class Df11Error(RuntimeError):
@@ -95,9 +94,6 @@ def _load():
         for fn in ("df11_histogram", "df11_build_codebook", "df11_build_luts",
                    "df11_encoded_sizes", "df11_encode", "df11_decode"):
             getattr(lib, fn).restype = ctypes.c_int
-        if hasattr(lib, "df11_balance_ranges"):
-            lib.df11_balance_ranges.argtypes = [_P, _U64, _P]
-            lib.df11_balance_ranges.restype = ctypes.c_int
         if hasattr(lib, "df11_decode_gemv"):
             lib.df11_gemv_workspace_bytes.argtypes = [ctypes.POINTER(DeviceStream)]
             lib.df11_gemv_workspace_bytes.restype = _U64
@@ -250,22 +246,10 @@ def to_device(enc: Encoded, device="cuda", status=None) -> DeviceEncoded:
     }
     if status is not None:
         t["status"] = status
-    return DeviceEncoded(_descriptor(enc.sizes, enc.codebook, t, enc.block_pos), t, enc.n)
+    return DeviceEncoded(_descriptor(enc.sizes, enc.codebook, t), t, enc.n)
 
 
-def balance_ranges(block_pos: np.ndarray) -> list[int]:
-    """First block of each of the 8 decode ranges (and n_blocks) for about
-    equal output counts per range, from the host copy of block_pos."""
-    bp = np.ascontiguousarray(block_pos, dtype=np.uint32)
-    starts = np.zeros(9, np.uint32)
-    _check("df11_balance_ranges",
-           _load().df11_balance_ranges(bp.ctypes.data, bp.size, starts.ctypes.data))
-    return [int(v) for v in starts]
-
-
-def _descriptor(sz: Sizes, cb: Codebook, t: dict, block_pos=None) -> DeviceStream:
-    """Descriptor of the device arrays in ``t``; with the host copy of
-    ``block_pos`` the decode ranges are balanced by output count."""
+def _descriptor(sz: Sizes, cb: Codebook, t: dict) -> DeviceStream:
     d = DeviceStream()
     d.stream, d.gaps, d.block_pos = t["stream"].data_ptr(), t["gaps"].data_ptr(), \
         t["block_pos"].data_ptr()
@@ -278,8 +262,6 @@ def _descriptor(sz: Sizes, cb: Codebook, t: dict, block_pos=None) -> DeviceStrea
     d.n, d.total_bits, d.last_start = sz.n, sz.total_bits, sz.last_start
     d.n_blocks, d.n_tables, d.max_len = sz.n_blocks, cb.n_tables, cb.max_len
     d.status = t["status"].data_ptr() if "status" in t else None
-    if block_pos is not None:
-        d.range_start[:] = balance_ranges(block_pos)
     return d
 
 

@@ -35,9 +35,9 @@
 //    route: decode the real bits again, straight into the tile;
 //  * the merge joins 8 exponents with 8 prefetched sign|mantissa bytes per
 //    lane and writes one 16-byte store;
-//  * blocks are split into 8 contiguous ranges, one per XCD (workgroups are
-//    dispatched round-robin over the XCDs), so neighbouring blocks, which
-//    share cache lines at their edges, meet in the same L2.
+//  * workgroups take blocks in runs of 8 from one window that moves through
+//    the whole stream, so all XCDs read and write near each other: one
+//    contiguous range per XCD put eight write fronts in step and was slower.
 #include <hip/hip_runtime.h>
 
 #include <atomic>
@@ -126,7 +126,6 @@ struct DecodeArgs {
     uint32_t n_blocks;
     uint32_t n_tables;
     uint32_t max_len;
-    uint32_t range_start[kXcds + 1];  // first block of each XCD's range, then n_blocks
 };
 
 // 8-bit table entry: leaf = symbol | (length - 1) << 8; pointer = 0x8000 |
@@ -560,23 +559,13 @@ __device__ __forceinline__ void decode_blocks(const DecodeArgs &a, Sink &sink) {
     const uint32_t tile_addr = lds_offset(tile);
     const uint8_t *lds_dec = reinterpret_cast<const uint8_t *>(dec_t);
 
-    // XCD-contiguous assignment: group g runs on XCD g % 8 (workgroups are
-    // dispatched round-robin over the XCDs) and owns the blocks
-    // range_lo + 8 slot + {0..7} + i * stride of that XCD's range.
-    const uint32_t xcd = blockIdx.x % kXcds;
+    // One window over the whole stream: group g owns the blocks
+    // 8 g + {0..7} + i * 8 * groups, so at any moment all XCDs work on one
+    // contiguous run of blocks.  (Splitting the blocks into one contiguous
+    // range per XCD was slower: eight write fronts moving in step through
+    // memory.)  `slot` tells apart the groups that share an XCD.
     const uint32_t slot = blockIdx.x / kXcds;
-    const uint32_t groups_per_xcd = gridDim.x / kXcds;
-    // (a switch with constant indices: indexing the kernel argument at run
-    // time would make the compiler copy it to scratch memory)
-    uint32_t range_lo = 0, range_hi = 0;
-    switch (xcd) {
-#define DF11_RANGE_CASE(x) \
-    case x: range_lo = a.range_start[x]; range_hi = a.range_start[x + 1]; break;
-        DF11_RANGE_CASE(0) DF11_RANGE_CASE(1) DF11_RANGE_CASE(2) DF11_RANGE_CASE(3)
-        DF11_RANGE_CASE(4) DF11_RANGE_CASE(5) DF11_RANGE_CASE(6) DF11_RANGE_CASE(7)
-#undef DF11_RANGE_CASE
-    }
-    const uint32_t stride = groups_per_xcd * kWavesPerGroup;
+    const uint32_t stride = gridDim.x * kWavesPerGroup;
 
     // slice g = 64 b + lane: its stream dwords are 2g..2g+2 and its 5-bit
     // gap field sits at bit 5 * lane of the block's 320 gap bits (dword 10 b)
@@ -589,9 +578,9 @@ __device__ __forceinline__ void decode_blocks(const DecodeArgs &a, Sink &sink) {
     // often simply takes fewer blocks.  (Workgroups keep fixed shares: global
     // atomics would queue every wave of an XCD on one address.)
     auto wg_block = [&](uint32_t i) {
-        const uint32_t blk = range_lo + slot * kWavesPerGroup + (i % kWavesPerGroup) +
+        const uint32_t blk = blockIdx.x * kWavesPerGroup + (i % kWavesPerGroup) +
                              (i / kWavesPerGroup) * stride;
-        return blk < range_hi ? blk : 0xFFFFFFFFu;
+        return blk < a.n_blocks ? blk : 0xFFFFFFFFu;
     };
     auto claim = [&]() {
         uint32_t v = 0;
@@ -945,21 +934,6 @@ int prepare(const df11_device_stream *s, uint16_t *out, DecodeArgs *a) {
     a->n_blocks = s->n_blocks;
     a->n_tables = s->n_tables;
     a->max_len = s->max_len;
-    // the caller's balanced ranges, or equal numbers of blocks
-    static_assert(DF11_RANGES == kXcds, "one block range per XCD");
-    if (s->range_start[kXcds] == 0) {
-        const uint32_t per = (s->n_blocks + kXcds - 1) / kXcds;
-        for (int r = 0; r <= kXcds; ++r) {
-            const uint64_t v = (uint64_t)per * r;
-            a->range_start[r] = (uint32_t)(v < s->n_blocks ? v : s->n_blocks);
-        }
-    } else {
-        if (s->range_start[0] != 0 || s->range_start[kXcds] != s->n_blocks) return DF11_ERR_FORMAT;
-        for (int r = 0; r <= kXcds; ++r) {
-            if (r && s->range_start[r] < s->range_start[r - 1]) return DF11_ERR_FORMAT;
-            a->range_start[r] = s->range_start[r];
-        }
-    }
     return DF11_OK;
 }
 

@@ -404,25 +404,3 @@ extern "C" int df11_encode(const uint16_t *bf16, uint64_t n, const df11_codebook
     out->lut_bytes = df11_internal::lut_image_bytes(cb->n_tables);
     return DF11_OK;
 }
-
-extern "C" int df11_balance_ranges(const uint32_t *block_pos, uint64_t block_pos_count,
-                                   uint32_t range_start[DF11_RANGES + 1]) {
-    if (!block_pos || !range_start || block_pos_count < 2 || block_pos_count - 1 > 0xFFFFFFFFull)
-        return DF11_ERR_ARG;
-    const uint64_t nb = block_pos_count - 1;
-    const uint64_t n = block_pos[nb];
-    for (int r = 0; r < DF11_RANGES; ++r) {
-        const uint64_t target = n * (uint64_t)r / DF11_RANGES;
-        // first block b with block_pos[b] >= target (block_pos is non-decreasing)
-        uint64_t lo = 0, hi = nb;
-        while (lo < hi) {
-            const uint64_t mid = (lo + hi) / 2;
-            if (block_pos[mid] < target) lo = mid + 1; else hi = mid;
-        }
-        range_start[r] = (uint32_t)lo;
-    }
-    range_start[DF11_RANGES] = (uint32_t)nb;
-    for (int r = 0; r < DF11_RANGES; ++r)
-        if (range_start[r] > range_start[r + 1]) return DF11_ERR_ARG;
-    return DF11_OK;
-}

@@ -183,7 +183,7 @@ class OffloadRunner:
         enc = self.encoded[i]
         views = {name: self.slots[slot][name][: self.host[i][name].numel()]
                  for name in self._ARRAYS}
-        return self._descriptor(enc.sizes, enc.codebook, views, enc.block_pos)
+        return self._descriptor(enc.sizes, enc.codebook, views)
 
     def run(self, consume=None):
         """Copy and decode every block in order; consume(i, bf16) (optional)

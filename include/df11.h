@@ -59,7 +59,6 @@ extern "C" {
 #define DF11_STREAM_GUARD 16
 #define DF11_MAX_TABLES 64
 #define DF11_MAX_N 0xFFFFFFFFull /* n must be below 2^32: block_pos is uint32 */
-#define DF11_RANGES 8 /* contiguous block ranges the decode splits a stream into */
 
 enum {
     DF11_OK = 0,
@@ -154,20 +153,7 @@ typedef struct df11_device_stream {
                           count differs from its block_pos range, or whose
                           block_pos range is malformed, adds 1 (the block's
                           output is then left unwritten or wrong) */
-    uint32_t range_start[DF11_RANGES + 1]; /* optional: first block of each of
-                          the ranges the GPU's 8 XCDs decode, and n_blocks
-                          (see df11_balance_ranges); all zero: equal numbers
-                          of blocks per range */
 } df11_device_stream;
-
-/* Block ranges with about equal numbers of output words (n / 8 each), from
- * the host copy of block_pos (block_pos_count = n_blocks + 1 entries):
- * range_start[r] = the first block whose first output index is at least
- * r * n / 8, range_start[8] = n_blocks.  Decode time follows the output
- * count more than the block count, so these ranges keep the XCDs evenly
- * loaded.  Errors: ARG. */
-int df11_balance_ranges(const uint32_t *block_pos, uint64_t block_pos_count,
-                        uint32_t range_start[DF11_RANGES + 1]);
 
 /* Decode on the GPU: out[0..n) = the original BF16 words, bit for bit.
  * Two-phase wave-per-block decode (section "Architecture", two-phase kernel):

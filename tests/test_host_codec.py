@@ -163,29 +163,6 @@ def test_decode_rejects_inconsistent_descriptor_on_host():
         assert lib.df11_decode(ctypes.byref(d), fake, None) == want, field
         setattr(d, field, saved)
     assert lib.df11_decode(ctypes.byref(d), fake + 2, None) == -1  # misaligned output
-    # block ranges: must start at 0, not decrease, and end at n_blocks
-    good = hd.balance_ranges(enc.block_pos)
-    for bad in ([1] + good[1:], good[:8] + [sz.n_blocks + 1], [0, 2, 1] + good[3:]):
-        if bad == good:
-            continue
-        d.range_start[:] = bad
-        assert lib.df11_decode(ctypes.byref(d), fake, None) == -5, bad
-    d.range_start[:] = [0] * 9
-
-
-@pytest.mark.parametrize("n,seed", [(10_000, 3), (200_000, 4), (5, 1)])
-def test_balance_ranges(n, seed):
-    """Range r starts at the first block whose first output index reaches
-    r * n / 8 (brute force over block_pos); the last entry is n_blocks."""
-    enc = hd.encode(wl.random_small(n, seed, "normal"))
-    bp = enc.block_pos.astype(np.int64)
-    nb = int(enc.sizes.n_blocks)
-    want = [next(b for b in range(nb + 1) if bp[b] >= (n * r) // 8) for r in range(8)] + [nb]
-    assert hd.balance_ranges(enc.block_pos) == want
-    lib = hd.library()
-    out = np.zeros(9, np.uint32)
-    assert lib.df11_balance_ranges(None, 5, out.ctypes.data) == -1
-    assert lib.df11_balance_ranges(enc.block_pos.ctypes.data, 1, out.ctypes.data) == -1
 
 
 # ---------------------------------------------------------------------------
