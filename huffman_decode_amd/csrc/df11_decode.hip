@@ -408,19 +408,19 @@ __device__ __forceinline__ uint32_t join1(uint32_t e, uint32_t sm) {
     return ((sm & 0x80u) << 8) | ((e & 0xFFu) << 7) | (sm & 0x7Fu);
 }
 
-// at least 6 waves per SIMD: keeps the register budget at 80 VGPRs, the
-// most that still lets 3 workgroups of 8 waves share a CU
 // What a decoded block's BF16 words go to.  The kernel body calls
 // begin(p0, base, j_lo, j_hi) once a block's output range is known (its full
 // 8-word groups are j in [j_lo, j_hi), group j at output index base + 8 j;
-// this lane handles j = lane + 64 i), group(pos, e8, sm8, i) for each full
-// group starting at output index pos, with i its round for this lane (the
-// first two rounds told apart, later ones passed as 2), one() for the single
-// head/tail words, and end(block) after the block.
+// this lane handles j = lane + 64 i); for each full group starting at output
+// index pos, f = fetch(pos) (issued early: the sink's own loads for that
+// group) and later group(pos, e8, sm8, f); one() for the single head/tail
+// words; and end(block) after the block.
 struct StoreSink {  // plain decode: BF16 words to out[]
     uint16_t *out;
+    struct Fetched {};
     __device__ __forceinline__ void begin(uint32_t, uint32_t, uint32_t, uint32_t) {}
-    __device__ __forceinline__ void group(uint32_t pos, uint2 e8, uint2 sm8, int) {
+    __device__ __forceinline__ Fetched fetch(uint32_t) const { return {}; }
+    __device__ __forceinline__ void group(uint32_t pos, uint2 e8, uint2 sm8, Fetched) {
         *reinterpret_cast<uint4 *>(out + pos) = join8(e8, sm8);
     }
     __device__ __forceinline__ void one(uint32_t pos, uint32_t e, uint32_t sm) {
@@ -450,18 +450,37 @@ struct GemvArgs {
 };
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
+// a.lo * b.lo + a.hi * b.hi + c for two BF16 pairs (v_dot2c_f32_bf16)
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                           __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+// x moved across lanes by one DPP control (lanes without a source read 0)
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ float dpp_f(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kCtrl, kRowMask, 0xF, false));
+}
+
+// Sum over the 64 lanes (every lane gets it) with the DPP row shifts and
+// broadcasts of wave_inclusive_sum, in a fixed order.
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
-    return v;
+    v += dpp_f<0x111, 0xF>(v);  // row_shr:1
+    v += dpp_f<0x112, 0xF>(v);  // row_shr:2
+    v += dpp_f<0x114, 0xF>(v);  // row_shr:4
+    v += dpp_f<0x118, 0xF>(v);  // row_shr:8
+    v += dpp_f<0x142, 0xA>(v);  // row_bcast:15
+    v += dpp_f<0x143, 0xC>(v);  // row_bcast:31
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), kWave - 1));
 }
 
 // The matrix table in LDS (copied from the kernel argument once per workgroup).
 struct GemvTable {
     uint32_t off[kGemvMaxMats + 1];
     uint32_t cols[kGemvMaxMats];
+    float inv_cols[kGemvMaxMats];  // 1 / cols, for the row of an output index
     uint32_t row0[kGemvMaxMats + 1];
     uint32_t xoff[kGemvMaxMats];
 };
@@ -482,7 +501,12 @@ struct DotSink {
         uint32_t m = 0;
         while (m + 1 < n_mats && p0 >= tab->off[m + 1]) ++m;
         const uint32_t c0 = tab->cols[m];
-        const uint32_t r = (p0 - tab->off[m]) / c0;
+        // row = q / c0 through the reciprocal: q < 2^32 and c0 >= 2048, so
+        // the float quotient is off by at most one, and one step fixes it
+        const uint32_t q = p0 - tab->off[m];
+        uint32_t r = (uint32_t)((float)q * tab->inv_cols[m]);
+        if ((uint64_t)r * c0 > q) --r;
+        else if (q - r * c0 >= c0) ++r;
         const uint32_t s0 = tab->off[m] + r * c0;
         grow = tab->row0[m] + r;
         d0 = tab->xoff[m] - s0;
@@ -505,18 +529,18 @@ struct DotSink {
     __device__ __forceinline__ uint32_t xi(uint32_t pos) const {
         return pos + d0 + (pos >= s1 ? dd1 : 0u) + (pos >= s2 ? dd2 : 0u);
     }
-    __device__ __forceinline__ void group(uint32_t pos, uint2 e8, uint2 sm8, int) {
+    typedef u32x4 Fetched;  // the group's 8 BF16 inputs
+    __device__ __forceinline__ Fetched fetch(uint32_t pos) const {
+        return *(const g_cu32x4 *)(x + xi(pos));
+    }
+    __device__ __forceinline__ void group(uint32_t pos, uint2 e8, uint2 sm8, Fetched xv) {
         const uint4 w = join8(e8, sm8);
-        const u32x4 xv = *(const g_cu32x4 *)(x + xi(pos));  // 8 BF16 inputs
-        // BF16 x BF16 products are exact in fp32; the sum is rounded per step
-        float v = bf16_lo(w.x) * bf16_lo(xv.x);
-        v = fmaf(bf16_hi(w.x), bf16_hi(xv.x), v);
-        v = fmaf(bf16_lo(w.y), bf16_lo(xv.y), v);
-        v = fmaf(bf16_hi(w.y), bf16_hi(xv.y), v);
-        v = fmaf(bf16_lo(w.z), bf16_lo(xv.z), v);
-        v = fmaf(bf16_hi(w.z), bf16_hi(xv.z), v);
-        v = fmaf(bf16_lo(w.w), bf16_lo(xv.w), v);
-        v = fmaf(bf16_hi(w.w), bf16_hi(xv.w), v);
+        // BF16 x BF16 products are exact in fp32; pairs of them are added to
+        // the running fp32 sum by the packed dot instruction
+        float v = dot2_bf16(w.x, xv.x, 0.0f);
+        v = dot2_bf16(w.y, xv.y, v);
+        v = dot2_bf16(w.z, xv.z, v);
+        v = dot2_bf16(w.w, xv.w, v);
         add(pos, v);
     }
     __device__ __forceinline__ void one(uint32_t pos, uint32_t e, uint32_t sm) {
@@ -528,6 +552,8 @@ struct DotSink {
     }
 };
 
+// at least 6 waves per SIMD: keeps the register budget at 80 VGPRs, the
+// most that still lets 3 workgroups of 8 waves share a CU
 #ifndef DF11_WAVES_PER_EU
 #define DF11_WAVES_PER_EU 6
 #endif
@@ -754,18 +780,28 @@ __device__ __forceinline__ void decode_blocks(const DecodeArgs &a, Sink &sink) {
             wave_lds_sync();
         }
         if (one_pass) {
-            // ---- merge with sign|mantissa, 8 BF16 per lane per group
+            // ---- merge with sign|mantissa, 8 BF16 per lane per group; the
+            // sink's loads for the first rounds are issued together first
+            // (a lane without a group there fetches for group full_lo)
+            typename Sink::Fetched fx[kPrefetchGroups];
+            if (full_lo < full_hi) {
+#pragma unroll
+                for (int i = 0; i < kPrefetchGroups; ++i) {
+                    const uint32_t j = lane + kWave * i;
+                    fx[i] = sink.fetch(base + 8 * (j >= full_lo && j < full_hi ? j : full_lo));
+                }
+            }
 #pragma unroll
             for (int i = 0; i < kPrefetchGroups; ++i) {
                 const uint32_t j = lane + kWave * i;
                 if (j >= full_lo && j < full_hi)
                     sink.group(base + 8 * j, *reinterpret_cast<const uint2 *>(tile + 8 * j), smv[i],
-                               i < 2 ? i : 2);
+                               fx[i]);
             }
             for (uint32_t j = lane + kWave * kPrefetchGroups; j < full_hi; j += kWave) {
                 const uint2 sm = *reinterpret_cast<const uint2 *>(a.signmant + base + 8 * j);
                 sink.group(base + 8 * j, *reinterpret_cast<const uint2 *>(tile + 8 * j), sm,
-                           kPrefetchGroups < 2 ? 2 : kPrefetchGroups);
+                           sink.fetch(base + 8 * j));
             }
             if (edge) sink.one(edge_i, tile[edge_i - base], edge_sm);
             wave_lds_sync();
@@ -779,7 +815,8 @@ __device__ __forceinline__ void decode_blocks(const DecodeArgs &a, Sink &sink) {
                 for (uint32_t j = r0 / 8 + lane; j < j_hi; j += kWave) {
                     if (j < full_lo || j >= full_hi) continue;  // edge groups: below
                     const uint2 sm = *reinterpret_cast<const uint2 *>(a.signmant + base + 8 * j);
-                    sink.group(base + 8 * j, *reinterpret_cast<const uint2 *>(tile + 8 * j - r0), sm, 2);
+                    sink.group(base + 8 * j, *reinterpret_cast<const uint2 *>(tile + 8 * j - r0), sm,
+                               sink.fetch(base + 8 * j));
                 }
                 const uint32_t er = edge_i - base - r0;
                 if (edge && er < (uint32_t)kTileCap) sink.one(edge_i, tile[er], edge_sm);
@@ -810,6 +847,7 @@ __global__ __launch_bounds__(kGroupThreads) DF11_OCCUPANCY_HINT void df11_gemv_k
 #pragma unroll
         for (int i = 0; i < kGemvMaxMats; ++i) {
             tab.cols[i] = g.cols[i];
+            tab.inv_cols[i] = g.cols[i] ? 1.0f / (float)g.cols[i] : 0.0f;
             tab.xoff[i] = g.xoff[i];
         }
     }
