@@ -70,11 +70,13 @@ constexpr int kStageMinCodes = 3;
 // exponent bytes one tile holds (the tile reuses the wave's staging region);
 // blocks with more symbols take several passes
 constexpr int kTileCap = 2560;
-// a lane's stores reach at most 3 bytes past its last code; a lane holds at
-// most 64 codes, so 4 + 63 * 40 + 67 bytes bound the staging stores of valid data
-constexpr int kTileBytes = kTileCap + 32;
+// phase 1 writes at most 71 bytes from a slot's start, whatever the data: a
+// step begins below bit 64 and every code takes at least one bit, so the
+// last step begins after at most 63 codes and stores two aligned dwords
+constexpr int kStageReach = 63 + 8;
+constexpr int kTileBytes = kTileCap + 40;
 static_assert(kTileCap % 8 == 0, "tile windows must stay 8-aligned");
-static_assert(kTileBytes >= kStageBase + 63 * kStageStride + 64 + 3, "staging must fit");
+static_assert(kTileBytes >= kStageBase + 63 * kStageStride + kStageReach, "staging must fit");
 static_assert(kStageStride % 4 == 0 && kStageBase % 4 == 0 && kTileBytes % 8 == 0,
               "staging dwords are aligned");
 static_assert(kStageStride >= kStageCodes + 4, "a full slot takes 4 stray bytes");
@@ -121,8 +123,9 @@ struct DecodeArgs {
     uint16_t *out;
     uint32_t *status;
     uint64_t n;
-    uint64_t total_bits;
-    uint64_t stop_bit;       // codes start strictly before this bit
+    // codes start strictly before bit 4096 stop_blk + stop_rem; the stream
+    // ends at bit 4096 end_blk + end_rem (block index and offset in it)
+    uint32_t stop_blk, stop_rem, end_blk, end_rem;
     uint32_t n_blocks;
     uint32_t n_tables;
     uint32_t max_len;
@@ -227,14 +230,12 @@ __device__ __forceinline__ uint32_t pad_ones(uint32_t d, int end, int base) {
 //
 // Stores are aligned: `cur` holds the slot's partly filled dword, and each
 // step ORs its symbols (unused table bytes are 0) in at the next byte and
-// stores the two dwords they can touch.  Stores are clamped to `clamp` so
-// that corrupt input cannot reach past the wave's region; valid data never
-// gets there.
+// stores the two dwords they can touch; they stay inside the wave's region
+// for any data (kStageReach).
 __device__ __forceinline__ uint32_t stage_codes(const uint8_t *lds_dec, const uint16_t *lut,
                                                 uint32_t n_tables, uint32_t d0, uint32_t d1,
                                                 uint32_t d2, uint32_t f0, uint32_t f1, uint32_t f2,
-                                                uint32_t pos, uint32_t stop, uint32_t slot,
-                                                uint32_t clamp) {
+                                                uint32_t pos, uint32_t stop, uint32_t slot) {
     // pre-shift by 3: window bits [3, 3+W) are the entry's byte offset
     const uint32_t e0 = f0 << 3, e1 = __builtin_amdgcn_alignbit(f1, f0, 29),
                    e2 = __builtin_amdgcn_alignbit(f2, f1, 29);
@@ -250,8 +251,7 @@ __device__ __forceinline__ uint32_t stage_codes(const uint8_t *lds_dec, const ui
             syms = e & 0xFFu;
             inc = leaf_len(e) | 0x10000u;
         }
-        uint32_t at = acc >> 16;
-        at = at < clamp ? at : clamp;
+        const uint32_t at = acc >> 16;
         // bits 13..17 of acc: pos >> 13 (always 0) | (byte address & 3) << 3
         const uint64_t t = (uint64_t)syms << __builtin_amdgcn_ubfe(acc, 13, 5);
         const uint32_t w0 = cur | (uint32_t)t, w1 = (uint32_t)(t >> 32);
@@ -701,21 +701,21 @@ __device__ __forceinline__ void decode_blocks(const DecodeArgs &a, Sink &sink) {
 
         const uint32_t gw = __builtin_amdgcn_alignbit(gw1, gw0, gap_shift);
         const uint32_t gap = gw & 31u, gap_next = (gw >> 5) & 31u;
-        // the stop bit and the stream end relative to this lane's slice, in
-        // 32 bits: wave-uniform 64-bit differences to the block start,
-        // clamped far outside the block's 4096 bits, minus the lane's offset
-        const uint64_t blk_bit = (uint64_t)b * (DF11_BLOCK_SLICES * DF11_SLICE_BITS);
-        auto near = [](int64_t v) {
-            return (int32_t)(v < -(1 << 30) ? -(1 << 30) : (v > (1 << 30) ? (1 << 30) : v));
+        // the stop bit and the stream end relative to this lane's slice:
+        // wave-uniform offsets from the block start, exact within a block of
+        // it and clamped far outside farther away, minus the lane's offset
+        auto from_block = [&](uint32_t blk, uint32_t rem) {
+            const int32_t d = (int32_t)(blk - b);  // block indices are below 2^27
+            return d > 1 ? (1 << 30) : (d < -1 ? -(1 << 30) : d * 4096 + (int32_t)rem);
         };
         const int32_t lane_bit = (int32_t)(lane * DF11_SLICE_BITS);
-        const int32_t rel = near((int64_t)a.stop_bit - (int64_t)blk_bit) - lane_bit;
+        const int32_t rel = from_block(a.stop_blk, a.stop_rem) - lane_bit;
         // codes of this lane start in [gap, lim); the last one ends at `end`:
         // the next slice's first code start, or the stream's end for the lane
         // holding the final code
         const uint32_t lim = rel <= 0 ? 0u : (rel >= 64 ? 64u : (uint32_t)rel);
         const uint32_t end = rel > 0 && rel <= 64
-                                 ? (uint32_t)(near((int64_t)a.total_bits - (int64_t)blk_bit) - lane_bit)
+                                 ? (uint32_t)(from_block(a.end_blk, a.end_rem) - lane_bit)
                                  : 64u + gap_next;
 
         // ---- phase 1: decode into the lane's staging slot, counting
@@ -723,7 +723,7 @@ __device__ __forceinline__ void decode_blocks(const DecodeArgs &a, Sink &sink) {
         const uint32_t cnt =
             lim ? stage_codes(lds_dec, lut, a.n_tables, d0, d1, d2, pad_ones(d0, (int)end, 0),
                               pad_ones(d1, (int)end, 32), pad_ones(d2, (int)end, 64), gap, lim,
-                              slot, tile_addr + kTileBytes - 8)
+                              slot)
                 : 0u;
 
         // wave-wide prefix sum of the counts
@@ -967,8 +967,11 @@ int prepare(const df11_device_stream *s, uint16_t *out, DecodeArgs *a) {
     a->out = out;
     a->status = s->status;
     a->n = s->n;
-    a->total_bits = s->total_bits;
-    a->stop_bit = s->last_start + 1;
+    static_assert(DF11_BLOCK_SLICES * DF11_SLICE_BITS == 4096, "4096-bit blocks");
+    a->stop_blk = (uint32_t)((s->last_start + 1) >> 12);
+    a->stop_rem = (uint32_t)((s->last_start + 1) & 4095);
+    a->end_blk = (uint32_t)(s->total_bits >> 12);
+    a->end_rem = (uint32_t)(s->total_bits & 4095);
     a->n_blocks = s->n_blocks;
     a->n_tables = s->n_tables;
     a->max_len = s->max_len;

@@ -28,7 +28,7 @@ STAGE_STRIDE = 40      # bytes of staging per lane
 STAGE_BASE = 4         # lane t's slot starts at byte 4 + 40 t of the region
 STAGE_CODES = 32       # codes a lane may stage; more sends the wave to the fallback
 MIN_CODES = 3          # fewer (before the block's last code) also does
-REGION = 2592          # LDS bytes per wave (staging and tile share them)
+REGION = 2600          # LDS bytes per wave (staging and tile share them)
 TILE_CAP = 2560
 STRAY = 0xEE           # value of the unfilled slots of a decode entry in this model
 
