@@ -107,6 +107,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(1))) const uint16_t g_cu16;
 typedef __attribute__((address_space(1))) const u32x4 g_cu32x4;
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(1))) const u32x2 g_cu32x2;
 typedef __attribute__((address_space(1))) f32x4 g_f32x4;
 
 __device__ __forceinline__ uint32_t lds_offset(const void *p) {
@@ -458,6 +460,13 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
                                            __builtin_bit_cast(bf16x2_t, b), c, false);
 }
 
+// 8 sign|mantissa bytes (8-byte aligned).  (Non-temporal loads here were
+// slower for the decode and no faster for the fused product.)
+__device__ __forceinline__ uint2 load_sm8(const uint8_t *p) {
+    const u32x2 v = *(g_cu32x2 *)p;
+    return make_uint2(v.x, v.y);
+}
+
 // x moved across lanes by one DPP control (lanes without a source read 0)
 template <int kCtrl, int kRowMask>
 __device__ __forceinline__ float dpp_f(float x) {
@@ -695,7 +704,7 @@ __device__ __forceinline__ void decode_blocks(const DecodeArgs &a, Sink &sink) {
         for (int i = 0; i < kPrefetchGroups; ++i) {
             const uint32_t j = lane + kWave * i;
             smv[i] = one_pass && j < groups
-                         ? *reinterpret_cast<const uint2 *>(a.signmant + base + 8 * j)
+                         ? load_sm8(a.signmant + base + 8 * j)
                          : make_uint2(0, 0);
         }
 
@@ -799,7 +808,7 @@ __device__ __forceinline__ void decode_blocks(const DecodeArgs &a, Sink &sink) {
                                fx[i]);
             }
             for (uint32_t j = lane + kWave * kPrefetchGroups; j < full_hi; j += kWave) {
-                const uint2 sm = *reinterpret_cast<const uint2 *>(a.signmant + base + 8 * j);
+                const uint2 sm = load_sm8(a.signmant + base + 8 * j);
                 sink.group(base + 8 * j, *reinterpret_cast<const uint2 *>(tile + 8 * j), sm,
                            sink.fetch(base + 8 * j));
             }
@@ -814,7 +823,7 @@ __device__ __forceinline__ void decode_blocks(const DecodeArgs &a, Sink &sink) {
                 const uint32_t j_hi = (r0 + kTileCap) / 8 < groups ? (r0 + kTileCap) / 8 : groups;
                 for (uint32_t j = r0 / 8 + lane; j < j_hi; j += kWave) {
                     if (j < full_lo || j >= full_hi) continue;  // edge groups: below
-                    const uint2 sm = *reinterpret_cast<const uint2 *>(a.signmant + base + 8 * j);
+                    const uint2 sm = load_sm8(a.signmant + base + 8 * j);
                     sink.group(base + 8 * j, *reinterpret_cast<const uint2 *>(tile + 8 * j - r0), sm,
                                sink.fetch(base + 8 * j));
                 }
