@@ -507,24 +507,33 @@ struct DotSink {
     uint32_t grow;       // global index of the block's first row
     float acc0, acc1, acc2;
     __device__ __forceinline__ void begin(uint32_t p0, uint32_t, uint32_t, uint32_t) {
-        uint32_t m = 0;
-        while (m + 1 < n_mats && p0 >= tab->off[m + 1]) ++m;
-        const uint32_t c0 = tab->cols[m];
+        // lane l reads table entry l once (all entries in one LDS round
+        // trip); the block's matrix m = the entries 1..n_mats-1 starting at
+        // or before p0, counted by ballot, and its fields come back by readlane
+        const uint32_t l = lane <= (uint32_t)kGemvMaxMats ? lane : (uint32_t)kGemvMaxMats;
+        const uint32_t lc = l < (uint32_t)kGemvMaxMats ? l : (uint32_t)kGemvMaxMats - 1;
+        const uint32_t off_l = tab->off[l], row0_l = tab->row0[l];
+        const uint32_t cols_l = tab->cols[lc], xoff_l = tab->xoff[lc];
+        const float inv_l = tab->inv_cols[lc];
+        const uint32_t m = (uint32_t)__builtin_popcountll(
+            __builtin_amdgcn_ballot_w64(lane >= 1 && lane < n_mats && off_l <= p0));
+        auto at = [](uint32_t v, uint32_t i) { return (uint32_t)__builtin_amdgcn_readlane((int)v, (int)i); };
+        const uint32_t c0 = at(cols_l, m), off_m = at(off_l, m);
         // row = q / c0 through the reciprocal: q < 2^32 and c0 >= 2048, so
         // the float quotient is off by at most one, and one step fixes it
-        const uint32_t q = p0 - tab->off[m];
-        uint32_t r = (uint32_t)((float)q * tab->inv_cols[m]);
+        const uint32_t q = p0 - off_m;
+        uint32_t r = (uint32_t)((float)q * __int_as_float((int)at(__float_as_uint(inv_l), m)));
         if ((uint64_t)r * c0 > q) --r;
         else if (q - r * c0 >= c0) ++r;
-        const uint32_t s0 = tab->off[m] + r * c0;
-        grow = tab->row0[m] + r;
-        d0 = tab->xoff[m] - s0;
+        const uint32_t s0 = off_m + r * c0;
+        grow = at(row0_l, m) + r;
+        d0 = at(xoff_l, m) - s0;
         s1 = s0 + c0;
-        const uint32_t m1 = (m + 1 < n_mats && s1 >= tab->off[m + 1]) ? m + 1 : m;
-        const uint32_t d1 = tab->xoff[m1] - s1;
-        s2 = s1 + tab->cols[m1];
-        const uint32_t m2 = (m1 + 1 < n_mats && s2 >= tab->off[m1 + 1]) ? m1 + 1 : m1;
-        const uint32_t d2 = tab->xoff[m2] - s2;
+        const uint32_t m1 = (m + 1 < n_mats && s1 >= at(off_l, m + 1)) ? m + 1 : m;
+        const uint32_t d1 = at(xoff_l, m1) - s1;
+        s2 = s1 + at(cols_l, m1);
+        const uint32_t m2 = (m1 + 1 < n_mats && s2 >= at(off_l, m1 + 1)) ? m1 + 1 : m1;
+        const uint32_t d2 = at(xoff_l, m2) - s2;
         dd1 = d1 - d0;
         dd2 = d2 - d1;
         acc0 = acc1 = acc2 = 0.0f;
@@ -869,6 +878,39 @@ __global__ __launch_bounds__(kGroupThreads) DF11_OCCUPANCY_HINT void df11_gemv_k
     decode_blocks(a, sink);
 }
 
+// The last block b in [0, nb) with block_pos[b] <= v (block_pos[0] = 0 <= v):
+// galloping from a guess made from the average block size, then bisection,
+// so a thread needs a few dependent loads instead of log2(nb).
+__device__ __forceinline__ uint32_t last_block_at_or_before(const uint32_t *block_pos,
+                                                           uint32_t nb, uint32_t v) {
+    const uint32_t n = block_pos[nb];
+    uint32_t g = n ? (uint32_t)((uint64_t)v * nb / n) : 0u;
+    g = g < nb ? g : nb - 1;
+    uint32_t lo, hi;  // block_pos[lo] <= v, and hi == nb or block_pos[hi] > v
+    if (block_pos[g] <= v) {
+        lo = g;
+        uint32_t step = 1;
+        while (lo + step < nb && block_pos[lo + step] <= v) {
+            lo += step;
+            step *= 2;
+        }
+        hi = lo + step < nb ? lo + step : nb;
+    } else {
+        hi = g;
+        uint32_t step = 1;
+        while (hi >= step && block_pos[hi - step] > v) {
+            hi -= step;
+            step *= 2;
+        }
+        lo = hi >= step ? hi - step : 0u;
+    }
+    while (hi - lo > 1) {
+        const uint32_t mid = lo + (hi - lo) / 2;
+        if (block_pos[mid] <= v) lo = mid; else hi = mid;
+    }
+    return lo;
+}
+
 // y of every row: the sums its blocks stored, in block order.
 __global__ __launch_bounds__(256) void df11_gemv_reduce_kernel(GemvArgs g, const uint32_t *block_pos,
                                                                uint32_t n_blocks) {
@@ -878,14 +920,12 @@ __global__ __launch_bounds__(256) void df11_gemv_reduce_kernel(GemvArgs g, const
     while (m + 1 < g.n_mats && row >= g.row0[m + 1]) ++m;
     const uint32_t r = row - g.row0[m];
     const uint32_t rs = g.off[m] + r * g.cols[m], re = rs + g.cols[m];
-    // the last block starting at or before rs: block_pos[lo] <= rs < block_pos[hi]
-    uint32_t lo = 0, hi = n_blocks;
-    while (hi - lo > 1) {
-        const uint32_t mid = (lo + hi) / 2;
-        if (block_pos[mid] <= rs) lo = mid; else hi = mid;
-    }
+    // the row's blocks: from the last one starting at or before rs to the
+    // last one starting before re (re - 1 is the row's last word)
+    const uint32_t lo = last_block_at_or_before(block_pos, n_blocks, rs);
+    const uint32_t hi = last_block_at_or_before(block_pos, n_blocks, re - 1) + 1;
     float sum = 0.0f;
-    for (uint32_t b = lo; b < n_blocks && block_pos[b] < re; ++b) {
+    for (uint32_t b = lo; b < hi; ++b) {
         const float4 p = g.partials[b];
         const uint32_t seg = row - __float_as_uint(p.w);
         sum += seg == 0 ? p.x : (seg == 1 ? p.y : (seg == 2 ? p.z : 0.0f));
