@@ -343,7 +343,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=None,
                     help="timed steps (default 100 for decode and copy, else 20)")
     ap.add_argument("--warmup", type=int, default=None,
-                    help="untimed steps first (default 10 for decode and copy, else 3)")
+                    help="untimed steps first (default 300 for decode and copy: the GPU's "
+                         "clocks take ~100 back-to-back launches to ramp up; else 3)")
     ap.add_argument("--workload", default="llama8b_block")
     ap.add_argument("--copies", type=int, default=3,
                     help="rotating encoded copies (defeats the Infinity Cache)")
@@ -362,7 +363,7 @@ def main() -> int:
     if args.steps is None:
         args.steps = 100 if fast else 20
     if args.warmup is None:
-        args.warmup = 10 if fast else 3
+        args.warmup = 300 if fast else 3
 
     if args.gpus != 1:
         print(json.dumps({"error": "df11_decode is measured on one GPU only (--gpus 1); "
