@@ -112,7 +112,7 @@ def run_copy(args) -> int:
     return 0
 
 
-def gemm_ratios(wlx, out, decode_ms, stream, batches=(1, 64), reps=10) -> dict:
+def gemm_ratios(wlx, out, decode_ms, stream, batches=(1, 2, 4, 64), reps=10) -> dict:
     """Decode time of the block over the time of the block's bf16 GEMMs
     (y = x W^T for each of its matrices, on the decoded weights) at each batch."""
     import torch
@@ -268,6 +268,30 @@ def fused_gemv(wlx, copies, stream, reps=20) -> dict:
     a.record(stream)
     for k in range(reps):
         hd.df11_decode_gemv(copies[k % len(copies)], mats, x, y, ws, stream)
+    b.record(stream)
+    torch.cuda.synchronize()
+    return {"fused_ms": round(a.elapsed_time(b) / reps, 5)}
+
+
+def fused_gemm(wlx, copies, stream, batch, reps=20) -> dict:
+    """y_b = W x_b for `batch` vectors straight from the DF11 stream
+    (df11_decode_gemm), timed over back-to-back launches like the decode."""
+    import numpy as np
+    import torch
+    import huffman_decode_amd as hd
+    shapes = [(m.rows, m.cols) for m in wlx.matrices]
+    mats, nx, ny = hd.gemv_matrices(shapes)
+    x = torch.from_numpy(np.random.default_rng(8).standard_normal((batch, nx)).astype(np.float32))
+    x = x.cuda().to(torch.bfloat16)
+    y = torch.empty(batch, ny, dtype=torch.float32, device="cuda")
+    ws = torch.empty(hd.df11_gemm_workspace_bytes(copies[0], batch), dtype=torch.uint8, device="cuda")
+    for k in range(3):
+        hd.df11_decode_gemm(copies[k % len(copies)], mats, x, y, ws, stream)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for k in range(reps):
+        hd.df11_decode_gemm(copies[k % len(copies)], mats, x, y, ws, stream)
     b.record(stream)
     torch.cuda.synchronize()
     return {"fused_ms": round(a.elapsed_time(b) / reps, 5)}
@@ -454,9 +478,17 @@ def main() -> int:
     }
     if not args.no_gemm:
         line["decode_vs_gemm"] = gemm_ratios(wlx, out, avg_ms, stream)
-        fg = fused_gemv(wlx, copies, stream)
-        fg["fused_over_bf16_gemv"] = round(fg["fused_ms"] / line["decode_vs_gemm"]["batch1"]["gemm_ms"], 4)
-        line["decode_vs_gemm"]["batch1_fused_decode_gemv"] = fg
+        # the fused product (df11_decode_gemv at batch 1, df11_decode_gemm at
+        # 2 and 4) against the BF16 GEMMs on resident weights and against
+        # decoding first and then running those GEMMs
+        fused = {}
+        for b in (1, 2, 4):
+            f = fused_gemv(wlx, copies, stream) if b == 1 else fused_gemm(wlx, copies, stream, b)
+            g = line["decode_vs_gemm"][f"batch{b}"]["gemm_ms"]
+            f["over_bf16_gemm"] = round(f["fused_ms"] / g, 4)
+            f["over_decode_then_gemm"] = round(f["fused_ms"] / (avg_ms + g), 4)
+            fused[f"batch{b}"] = f
+        line["decode_vs_gemm"]["fused"] = fused
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wlx, enc)
     print(json.dumps(line), flush=True)

@@ -100,6 +100,12 @@ def _load():
             lib.df11_decode_gemv.argtypes = [ctypes.POINTER(DeviceStream),
                                              ctypes.POINTER(GemvMatrix), _U32, _P, _P, _P, _U64, _P]
             lib.df11_decode_gemv.restype = ctypes.c_int
+        if hasattr(lib, "df11_decode_gemm"):
+            lib.df11_gemm_workspace_bytes.argtypes = [ctypes.POINTER(DeviceStream), _U32]
+            lib.df11_gemm_workspace_bytes.restype = _U64
+            lib.df11_decode_gemm.argtypes = [ctypes.POINTER(DeviceStream), ctypes.POINTER(GemvMatrix),
+                                             _U32, _P, _U32, _U64, _P, _U64, _P, _U64, _P]
+            lib.df11_decode_gemm.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -326,3 +332,29 @@ def df11_decode_gemv(dev: DeviceEncoded, mats: list[GemvMatrix], x, y, workspace
     _check("df11_decode_gemv", _load().df11_decode_gemv(
         ctypes.byref(dev.desc), arr, len(mats), x.data_ptr(), y.data_ptr(),
         workspace.data_ptr(), nbytes, stream.cuda_stream))
+
+
+def df11_gemm_workspace_bytes(dev: DeviceEncoded, batch: int) -> int:
+    return int(_load().df11_gemm_workspace_bytes(ctypes.byref(dev.desc), batch))
+
+
+def df11_decode_gemm(dev: DeviceEncoded, mats: list[GemvMatrix], x, y, workspace,
+                     stream=None) -> None:
+    """Enqueue y[b] = W x[b] for every matrix of ``dev`` and every row b of x
+    (x a [batch, nx] bfloat16 and y a [batch, ny] float32 CUDA tensor, batch
+    1..8, rows strided by their row stride; workspace a CUDA tensor of at
+    least df11_gemm_workspace_bytes(dev, batch) bytes)."""
+    import torch
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be a [batch, nx] bfloat16 tensor with unit column stride")
+    if y.dtype != torch.float32 or y.dim() != 2 or y.stride(1) != 1:
+        raise ValueError("y must be a [batch, ny] float32 tensor with unit column stride")
+    if x.shape[0] != y.shape[0]:
+        raise ValueError("x and y must hold the same number of vectors")
+    if stream is None:
+        stream = torch.cuda.current_stream(y.device)
+    arr = (GemvMatrix * len(mats))(*mats)
+    nbytes = workspace.numel() * workspace.element_size()
+    _check("df11_decode_gemm", _load().df11_decode_gemm(
+        ctypes.byref(dev.desc), arr, len(mats), x.data_ptr(), x.shape[0], x.stride(0),
+        y.data_ptr(), y.stride(0), workspace.data_ptr(), nbytes, stream.cuda_stream))

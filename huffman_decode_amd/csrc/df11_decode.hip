@@ -108,6 +108,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(1))) const uint16_t g_cu16;
 typedef __attribute__((address_space(1))) const u32x4 g_cu32x4;
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(1))) float g_f32;
 typedef __attribute__((address_space(1))) const u32x2 g_cu32x2;
 typedef __attribute__((address_space(1))) f32x4 g_f32x4;
 
@@ -411,8 +412,9 @@ __device__ __forceinline__ uint32_t join1(uint32_t e, uint32_t sm) {
 }
 
 // What a decoded block's BF16 words go to.  The kernel body calls
-// begin(p0, base, j_lo, j_hi) once a block's output range is known (its full
-// 8-word groups are j in [j_lo, j_hi), group j at output index base + 8 j;
+// begin(p0, p1, base, j_lo, j_hi) once a block's output range [p0, p1) is
+// known (its full 8-word groups are j in [j_lo, j_hi), group j at output
+// index base + 8 j;
 // this lane handles j = lane + 64 i); for each full group starting at output
 // index pos, f = fetch(pos) (issued early: the sink's own loads for that
 // group) and later group(pos, e8, sm8, f); one() for the single head/tail
@@ -420,7 +422,8 @@ __device__ __forceinline__ uint32_t join1(uint32_t e, uint32_t sm) {
 struct StoreSink {  // plain decode: BF16 words to out[]
     uint16_t *out;
     struct Fetched {};
-    __device__ __forceinline__ void begin(uint32_t, uint32_t, uint32_t, uint32_t) {}
+    static constexpr int kEarlyFetch = 0;
+    __device__ __forceinline__ void begin(uint32_t, uint32_t, uint32_t, uint32_t, uint32_t) {}
     __device__ __forceinline__ Fetched fetch(uint32_t) const { return {}; }
     __device__ __forceinline__ void group(uint32_t pos, uint2 e8, uint2 sm8, Fetched) {
         *reinterpret_cast<uint4 *>(out + pos) = join8(e8, sm8);
@@ -431,18 +434,27 @@ struct StoreSink {  // plain decode: BF16 words to out[]
     __device__ __forceinline__ void end(uint32_t, uint32_t) {}
 };
 
-// Fused GEMV: y = W x for row-major matrices laid end to end in the decoded
-// output.  Every matrix row holds at least 2048 words, so one block's output
-// (at most 4096 words) touches at most three rows; a wave sums its products
-// per row and stores the three sums and the first row's index per block.
-// df11_gemv_reduce_kernel then adds those per row in block order, so the
+// Fused product: y_b = W x_b for row-major matrices laid end to end in the
+// decoded output, for up to 8 input vectors x_b at once.  Every matrix row
+// holds at least 2048 words, so one block's output (at most 4096 words)
+// touches at most three rows; a wave sums its products per row and input
+// vector and stores those sums and the first row's index per block.
+// df11_gemm_reduce_kernel then adds them per row in block order, so the
 // result does not depend on scheduling.
 constexpr int kGemvMaxMats = 16;
 constexpr uint32_t kGemvMinCols = 2048;
+constexpr int kGemmMaxBatch = 8;
+// floats of partial sums per block for a batch capacity of kB vectors: three
+// rows x kB sums, then the first row's index, rounded up to whole float4s
+constexpr int partial_floats(int kB) { return (3 * kB + 1 + 3) / 4 * 4; }
 struct GemvArgs {
-    const uint16_t *x;      // all matrices' BF16 x vectors, matrix m's at x + xoff[m]
-    float *y;               // all matrices' results, matrix m's at y + yoff[m]
-    float4 *partials;       // per block: row sums of its first three rows, first row (bits)
+    const uint16_t *x;      // all matrices' BF16 x vectors, matrix m's at x + xoff[m];
+                            // vector b at x + b * x_stride
+    float *y;               // all matrices' results, matrix m's at y + yoff[m];
+                            // vector b's at y + b * y_stride
+    float *partials;        // per block: partial_floats(capacity) floats
+    uint64_t x_stride, y_stride;
+    uint32_t batch;         // vectors in use, 1..capacity
     uint32_t n_mats;
     uint32_t off[kGemvMaxMats + 1];   // first output index of each matrix; off[n_mats] = n
     uint32_t cols[kGemvMaxMats];
@@ -494,19 +506,25 @@ struct GemvTable {
     uint32_t xoff[kGemvMaxMats];
 };
 
+template <int kB>
 struct DotSink {
+    // inputs for a lane's first groups are fetched ahead of the joins only
+    // while they fit the register budget
+    static constexpr int kEarlyFetch = kB == 1;
     const GemvTable *tab;  // in LDS
     const g_cu16 *x;       // BF16
     g_f32x4 *partials;
-    uint32_t n_mats, lane;
+    uint64_t x_stride;
+    uint32_t batch, n_mats, lane;
     uint32_t s1, s2;     // first output index of the block's second and third row
     // x index - output index: d0 in the first row, + dd1 from the second,
     // + dd2 from the third (selecting among three fields would become an
     // indexed load and keep this object in scratch memory)
     uint32_t d0, dd1, dd2;
     uint32_t grow;       // global index of the block's first row
-    float acc0, acc1, acc2;
-    __device__ __forceinline__ void begin(uint32_t p0, uint32_t, uint32_t, uint32_t) {
+    bool row1, row2;     // the block reaches its second / third row
+    float acc0[kB], acc1[kB], acc2[kB];
+    __device__ __forceinline__ void begin(uint32_t p0, uint32_t p1, uint32_t, uint32_t, uint32_t) {
         // lane l reads table entry l once (all entries in one LDS round
         // trip); the block's matrix m = the entries 1..n_mats-1 starting at
         // or before p0, counted by ballot, and its fields come back by readlane
@@ -536,37 +554,84 @@ struct DotSink {
         const uint32_t d2 = at(xoff_l, m2) - s2;
         dd1 = d1 - d0;
         dd2 = d2 - d1;
-        acc0 = acc1 = acc2 = 0.0f;
+        row1 = s1 < p1;
+        row2 = s2 < p1;
+#pragma unroll
+        for (int b = 0; b < kB; ++b) acc0[b] = acc1[b] = acc2[b] = 0.0f;
     }
-    __device__ __forceinline__ void add(uint32_t pos, float v) {
-        acc0 += pos < s1 ? v : 0.0f;
-        acc1 += pos >= s1 && pos < s2 ? v : 0.0f;
-        acc2 += pos >= s2 ? v : 0.0f;
+    __device__ __forceinline__ void add(uint32_t pos, int b, float v) {
+        acc0[b] += pos < s1 ? v : 0.0f;
+        acc1[b] += pos >= s1 && pos < s2 ? v : 0.0f;
+        acc2[b] += pos >= s2 ? v : 0.0f;
     }
     // x index of output index pos; modular 32-bit arithmetic keeps it exact
     __device__ __forceinline__ uint32_t xi(uint32_t pos) const {
         return pos + d0 + (pos >= s1 ? dd1 : 0u) + (pos >= s2 ? dd2 : 0u);
     }
-    typedef u32x4 Fetched;  // the group's 8 BF16 inputs
+    struct Fetched {
+        u32x4 v[kB];  // the group's 8 BF16 inputs of each vector
+    };
     __device__ __forceinline__ Fetched fetch(uint32_t pos) const {
-        return *(const g_cu32x4 *)(x + xi(pos));
+        Fetched f;
+        const g_cu16 *p = x + xi(pos);
+#pragma unroll
+        for (int b = 0; b < kB; ++b)
+            f.v[b] = b == 0 || (uint32_t)b < batch ? *(const g_cu32x4 *)(p + b * x_stride)
+                                                  : u32x4{0, 0, 0, 0};
+        return f;
     }
-    __device__ __forceinline__ void group(uint32_t pos, uint2 e8, uint2 sm8, Fetched xv) {
+    __device__ __forceinline__ void group(uint32_t pos, uint2 e8, uint2 sm8, const Fetched &f) {
         const uint4 w = join8(e8, sm8);
         // BF16 x BF16 products are exact in fp32; pairs of them are added to
         // the running fp32 sum by the packed dot instruction
-        float v = dot2_bf16(w.x, xv.x, 0.0f);
-        v = dot2_bf16(w.y, xv.y, v);
-        v = dot2_bf16(w.z, xv.z, v);
-        v = dot2_bf16(w.w, xv.w, v);
-        add(pos, v);
+#pragma unroll
+        for (int b = 0; b < kB; ++b) {
+            float v = dot2_bf16(w.x, f.v[b].x, 0.0f);
+            v = dot2_bf16(w.y, f.v[b].y, v);
+            v = dot2_bf16(w.z, f.v[b].z, v);
+            v = dot2_bf16(w.w, f.v[b].w, v);
+            add(pos, b, v);
+        }
     }
     __device__ __forceinline__ void one(uint32_t pos, uint32_t e, uint32_t sm) {
-        add(pos, bf16_lo(join1(e, sm)) * bf16_lo(x[xi(pos)]));
+        const float w = bf16_lo(join1(e, sm));
+        const g_cu16 *p = x + xi(pos);
+#pragma unroll
+        for (int b = 0; b < kB; ++b)
+            if (b == 0 || (uint32_t)b < batch) add(pos, b, w * bf16_lo(p[b * x_stride]));
     }
     __device__ __forceinline__ void end(uint32_t blk, uint32_t) {
-        const float t0 = wave_sum(acc0), t1 = wave_sum(acc1), t2 = wave_sum(acc2);
-        if (lane == 0) partials[blk] = f32x4{t0, t1, t2, __uint_as_float(grow)};
+        // sums only for the rows the block reaches: the reduce reads a
+        // block's slot for a row only if the block holds words of that row
+        if constexpr (kB == 1) {
+            const float t0 = wave_sum(acc0[0]);
+            const float t1 = row1 ? wave_sum(acc1[0]) : 0.0f;
+            const float t2 = row2 ? wave_sum(acc2[0]) : 0.0f;
+            if (lane == 0) partials[blk] = f32x4{t0, t1, t2, __uint_as_float(grow)};
+        } else {
+            // one sum at a time, stored by lane 0 as soon as it is formed
+            g_f32 *dst = (g_f32 *)partials + (uint64_t)blk * partial_floats(kB);
+            if (lane == 0) dst[3 * kB] = __uint_as_float(grow);
+#pragma unroll
+            for (int b = 0; b < kB; ++b) {
+                const float t = wave_sum(acc0[b]);
+                if (lane == 0) dst[b] = t;
+            }
+            if (row1) {
+#pragma unroll
+                for (int b = 0; b < kB; ++b) {
+                    const float t = wave_sum(acc1[b]);
+                    if (lane == 0) dst[kB + b] = t;
+                }
+            }
+            if (row2) {
+#pragma unroll
+                for (int b = 0; b < kB; ++b) {
+                    const float t = wave_sum(acc2[b]);
+                    if (lane == 0) dst[2 * kB + b] = t;
+                }
+            }
+        }
     }
 };
 
@@ -766,12 +831,12 @@ __device__ __forceinline__ void decode_blocks(const DecodeArgs &a, Sink &sink) {
         if (!sane || total != p1 - p0) {
             if (lane == 0 && a.status) atomicAdd(a.status, 1u);
             if (sane) {  // leave a defined (empty) result for the block
-                sink.begin(p0, base, 0, 0);
+                sink.begin(p0, p1, base, 0, 0);
                 sink.end(cur_blk, lane);
             }
             continue;
         }
-        sink.begin(p0, base, one_pass ? full_lo : 0u, one_pass ? full_hi : 0u);
+        sink.begin(p0, p1, base, one_pass ? full_lo : 0u, one_pass ? full_hi : 0u);
         const uint32_t at = (p0 - base) + excl;  // tile position of this lane's first symbol
         const uint32_t stop = lim ? lim : 0u;
         const uint32_t start = lim ? gap : 0u;
@@ -798,23 +863,34 @@ __device__ __forceinline__ void decode_blocks(const DecodeArgs &a, Sink &sink) {
             wave_lds_sync();
         }
         if (one_pass) {
-            // ---- merge with sign|mantissa, 8 BF16 per lane per group; the
-            // sink's loads for the first rounds are issued together first
-            // (a lane without a group there fetches for group full_lo)
-            typename Sink::Fetched fx[kPrefetchGroups];
-            if (full_lo < full_hi) {
+            // ---- merge with sign|mantissa, 8 BF16 per lane per group; where
+            // the sink allows, its loads for the first rounds are issued
+            // together first (a lane without a group there fetches for group
+            // full_lo)
+            if constexpr (Sink::kEarlyFetch != 0) {
+                typename Sink::Fetched fx[kPrefetchGroups];
+                if (full_lo < full_hi) {
+#pragma unroll
+                    for (int i = 0; i < kPrefetchGroups; ++i) {
+                        const uint32_t j = lane + kWave * i;
+                        fx[i] = sink.fetch(base + 8 * (j >= full_lo && j < full_hi ? j : full_lo));
+                    }
+                }
 #pragma unroll
                 for (int i = 0; i < kPrefetchGroups; ++i) {
                     const uint32_t j = lane + kWave * i;
-                    fx[i] = sink.fetch(base + 8 * (j >= full_lo && j < full_hi ? j : full_lo));
+                    if (j >= full_lo && j < full_hi)
+                        sink.group(base + 8 * j, *reinterpret_cast<const uint2 *>(tile + 8 * j),
+                                   smv[i], fx[i]);
                 }
-            }
+            } else {
 #pragma unroll
-            for (int i = 0; i < kPrefetchGroups; ++i) {
-                const uint32_t j = lane + kWave * i;
-                if (j >= full_lo && j < full_hi)
-                    sink.group(base + 8 * j, *reinterpret_cast<const uint2 *>(tile + 8 * j), smv[i],
-                               fx[i]);
+                for (int i = 0; i < kPrefetchGroups; ++i) {
+                    const uint32_t j = lane + kWave * i;
+                    if (j >= full_lo && j < full_hi)
+                        sink.group(base + 8 * j, *reinterpret_cast<const uint2 *>(tile + 8 * j),
+                                   smv[i], sink.fetch(base + 8 * j));
+                }
             }
             for (uint32_t j = lane + kWave * kPrefetchGroups; j < full_hi; j += kWave) {
                 const uint2 sm = load_sm8(a.signmant + base + 8 * j);
@@ -850,8 +926,17 @@ __global__ __launch_bounds__(kGroupThreads) DF11_OCCUPANCY_HINT void df11_decode
     decode_blocks(a, sink);
 }
 
-__global__ __launch_bounds__(kGroupThreads) DF11_OCCUPANCY_HINT void df11_gemv_kernel(DecodeArgs a,
-                                                                                    GemvArgs g) {
+// Occupancy of the fused product kernel for capacity kB.  Up to 2 vectors
+// it keeps the decode's budget of 80 VGPRs (3 workgroups per CU); 4 and 8
+// vectors need more registers and run 2 workgroups per CU.
+template <int kB> struct GemmOccupancy {
+    static constexpr int kWavesPerEu = kB <= 2 ? DF11_WAVES_PER_EU : 4;
+};
+
+template <int kB>
+__global__ __launch_bounds__(kGroupThreads)
+__attribute__((amdgpu_waves_per_eu(GemmOccupancy<kB>::kWavesPerEu)))
+void df11_gemm_kernel(DecodeArgs a, GemvArgs g) {
     // the matrix table goes to LDS with constant indices (indexing the kernel
     // argument at run time would make the compiler copy it to scratch); the
     // first barrier in decode_blocks publishes it
@@ -869,10 +954,12 @@ __global__ __launch_bounds__(kGroupThreads) DF11_OCCUPANCY_HINT void df11_gemv_k
             tab.xoff[i] = g.xoff[i];
         }
     }
-    DotSink sink;
+    DotSink<kB> sink;
     sink.tab = &tab;
     sink.x = (const g_cu16 *)g.x;
     sink.partials = (g_f32x4 *)g.partials;
+    sink.x_stride = g.x_stride;
+    sink.batch = g.batch;
     sink.n_mats = g.n_mats;
     sink.lane = threadIdx.x % kWave;
     decode_blocks(a, sink);
@@ -911,8 +998,9 @@ __device__ __forceinline__ uint32_t last_block_at_or_before(const uint32_t *bloc
     return lo;
 }
 
-// y of every row: the sums its blocks stored, in block order.
-__global__ __launch_bounds__(256) void df11_gemv_reduce_kernel(GemvArgs g, const uint32_t *block_pos,
+// y of every row and vector: the sums its blocks stored, in block order.
+template <int kB>
+__global__ __launch_bounds__(256) void df11_gemm_reduce_kernel(GemvArgs g, const uint32_t *block_pos,
                                                                uint32_t n_blocks) {
     const uint32_t row = blockIdx.x * 256 + threadIdx.x;
     if (row >= g.row0[g.n_mats]) return;
@@ -921,22 +1009,31 @@ __global__ __launch_bounds__(256) void df11_gemv_reduce_kernel(GemvArgs g, const
     const uint32_t r = row - g.row0[m];
     const uint32_t rs = g.off[m] + r * g.cols[m], re = rs + g.cols[m];
     // the row's blocks: from the last one starting at or before rs to the
-    // last one starting before re (re - 1 is the row's last word)
+    // last one starting before re (re - 1 is the row's last word); each of
+    // them holds words of the row, so its slot for the row was written
     const uint32_t lo = last_block_at_or_before(block_pos, n_blocks, rs);
     const uint32_t hi = last_block_at_or_before(block_pos, n_blocks, re - 1) + 1;
-    float sum = 0.0f;
-    for (uint32_t b = lo; b < hi; ++b) {
-        const float4 p = g.partials[b];
-        const uint32_t seg = row - __float_as_uint(p.w);
-        sum += seg == 0 ? p.x : (seg == 1 ? p.y : (seg == 2 ? p.z : 0.0f));
+    constexpr int kP = partial_floats(kB);
+    float sum[kB];
+#pragma unroll
+    for (int b = 0; b < kB; ++b) sum[b] = 0.0f;
+    for (uint32_t blk = lo; blk < hi; ++blk) {
+        const float *p = g.partials + (uint64_t)blk * kP;
+        const uint32_t seg = row - __float_as_uint(p[3 * kB]);  // 0, 1 or 2
+        if (seg < 3) {
+#pragma unroll
+            for (int b = 0; b < kB; ++b) sum[b] += p[seg * kB + b];
+        }
     }
-    g.y[g.yoff[m] + r] = sum;
+#pragma unroll
+    for (int b = 0; b < kB; ++b)
+        if ((uint32_t)b < g.batch) g.y[b * g.y_stride + g.yoff[m] + r] = sum[b];
 }
 
 // Launch shape per device: compute units and, per kernel, resident
 // workgroups per CU for each table count (the LDS footprint depends on it).
 constexpr int kMaxDevices = 16;
-constexpr int kKernels = 2;  // 0: decode, 1: fused GEMV
+constexpr int kKernels = 5;  // 0: decode, 1..4: fused product for 1, 2, 4, 8 vectors
 std::atomic<int> g_cus[kMaxDevices];
 std::atomic<int> g_occ[kKernels][kMaxDevices][DF11_MAX_TABLES + 1];
 
@@ -1044,27 +1141,60 @@ extern "C" int df11_decode(const df11_device_stream *s, uint16_t *out, void *hip
     return hipGetLastError() == hipSuccess ? DF11_OK : DF11_ERR_HIP;
 }
 
-extern "C" uint64_t df11_gemv_workspace_bytes(const df11_device_stream *s) {
-    return s ? 16ull * s->n_blocks : 0;
+// batch capacity (1, 2, 4 or 8) used for a batch of 1..8 vectors
+static int gemm_capacity(uint32_t batch) { return batch <= 1 ? 1 : batch <= 2 ? 2 : batch <= 4 ? 4 : 8; }
+
+extern "C" uint64_t df11_gemm_workspace_bytes(const df11_device_stream *s, uint32_t batch) {
+    if (!s || batch < 1 || batch > (uint32_t)kGemmMaxBatch) return 0;
+    return 4ull * partial_floats(gemm_capacity(batch)) * s->n_blocks;
 }
 
-extern "C" int df11_decode_gemv(const df11_device_stream *s, const df11_gemv_matrix *mats,
-                                uint32_t n_mats, const uint16_t *x, float *y, void *workspace,
+extern "C" uint64_t df11_gemv_workspace_bytes(const df11_device_stream *s) {
+    return df11_gemm_workspace_bytes(s, 1);
+}
+
+template <int kB>
+static int launch_gemm(const df11_device_stream *s, const DecodeArgs &a, const GemvArgs &g,
+                       uint64_t rows, hipStream_t hs) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return DF11_ERR_HIP;
+    int groups = 0;
+    const int which = kB == 1 ? 1 : kB == 2 ? 2 : kB == 4 ? 3 : 4;
+    int st = launch_groups(df11_gemm_kernel<kB>, which, dev, s->n_tables, s->n_blocks, s->max_groups,
+                           &groups);
+    if (st != DF11_OK) return st;
+    hipLaunchKernelGGL(df11_gemm_kernel<kB>, dim3(groups), dim3(kGroupThreads),
+                       lds_bytes(s->n_tables), hs, a, g);
+    hipLaunchKernelGGL(df11_gemm_reduce_kernel<kB>, dim3((uint32_t)((rows + 255) / 256)), dim3(256),
+                       0, hs, g, a.block_pos, a.n_blocks);
+    return hipGetLastError() == hipSuccess ? DF11_OK : DF11_ERR_HIP;
+}
+
+extern "C" int df11_decode_gemm(const df11_device_stream *s, const df11_gemv_matrix *mats,
+                                uint32_t n_mats, const uint16_t *x, uint32_t batch,
+                                uint64_t x_stride, float *y, uint64_t y_stride, void *workspace,
                                 uint64_t workspace_bytes, void *hip_stream) {
     if (!mats || !x || !y || !workspace) return DF11_ERR_ARG;
     DecodeArgs a;
     int st = prepare(s, nullptr, &a);
     if (st != DF11_OK) return st;
-    if (n_mats < 1 || n_mats > (uint32_t)kGemvMaxMats || !aligned(x, 16) || !aligned(y, 4) ||
+    if (n_mats < 1 || n_mats > (uint32_t)kGemvMaxMats || batch < 1 ||
+        batch > (uint32_t)kGemmMaxBatch || !aligned(x, 16) || !aligned(y, 4) ||
         !aligned(workspace, 16))
         return DF11_ERR_ARG;
-    if (workspace_bytes < df11_gemv_workspace_bytes(s)) return DF11_ERR_BUFSIZE;
+    // vector b's inputs start 16-byte aligned; offsets stay 32-bit
+    if (batch > 1 && (x_stride % 8 != 0 || x_stride >= (1ull << 32) || y_stride >= (1ull << 32)))
+        return DF11_ERR_ARG;
+    if (workspace_bytes < df11_gemm_workspace_bytes(s, batch)) return DF11_ERR_BUFSIZE;
     GemvArgs g;
     g.x = x;
     g.y = y;
-    g.partials = static_cast<float4 *>(workspace);
+    g.partials = static_cast<float *>(workspace);
+    g.x_stride = batch > 1 ? x_stride : 0;
+    g.y_stride = batch > 1 ? y_stride : 0;
+    g.batch = batch;
     g.n_mats = n_mats;
-    uint64_t off = 0, rows = 0;
+    uint64_t off = 0, rows = 0, x_end = 0, y_end = 0;
     for (uint32_t m = 0; m < n_mats; ++m) {
         const df11_gemv_matrix &mm = mats[m];
         // matrices end to end in output order; rows long enough that a block
@@ -1079,20 +1209,27 @@ extern "C" int df11_decode_gemv(const df11_device_stream *s, const df11_gemv_mat
         g.yoff[m] = mm.y_offset;
         off += (uint64_t)mm.rows * mm.cols;
         rows += mm.rows;
+        const uint64_t xe = (uint64_t)mm.x_offset + mm.cols, ye = (uint64_t)mm.y_offset + mm.rows;
+        x_end = xe > x_end ? xe : x_end;
+        y_end = ye > y_end ? ye : y_end;
         if (off > s->n || rows >= 0x80000000ull) return DF11_ERR_ARG;
     }
     if (off != s->n) return DF11_ERR_ARG;
+    // each vector's inputs and results end before the next vector's begin
+    if (batch > 1 && (x_stride < x_end || y_stride < y_end)) return DF11_ERR_ARG;
     g.off[n_mats] = (uint32_t)off;
     g.row0[n_mats] = (uint32_t)rows;
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return DF11_ERR_HIP;
-    int groups = 0;
-    st = launch_groups(df11_gemv_kernel, 1, dev, s->n_tables, s->n_blocks, s->max_groups, &groups);
-    if (st != DF11_OK) return st;
     const hipStream_t hs = static_cast<hipStream_t>(hip_stream);
-    hipLaunchKernelGGL(df11_gemv_kernel, dim3(groups), dim3(kGroupThreads), lds_bytes(s->n_tables),
-                       hs, a, g);
-    hipLaunchKernelGGL(df11_gemv_reduce_kernel, dim3((uint32_t)((rows + 255) / 256)), dim3(256), 0,
-                       hs, g, a.block_pos, a.n_blocks);
-    return hipGetLastError() == hipSuccess ? DF11_OK : DF11_ERR_HIP;
+    switch (gemm_capacity(batch)) {
+    case 1: return launch_gemm<1>(s, a, g, rows, hs);
+    case 2: return launch_gemm<2>(s, a, g, rows, hs);
+    case 4: return launch_gemm<4>(s, a, g, rows, hs);
+    default: return launch_gemm<8>(s, a, g, rows, hs);
+    }
+}
+
+extern "C" int df11_decode_gemv(const df11_device_stream *s, const df11_gemv_matrix *mats,
+                                uint32_t n_mats, const uint16_t *x, float *y, void *workspace,
+                                uint64_t workspace_bytes, void *hip_stream) {
+    return df11_decode_gemm(s, mats, n_mats, x, 1, 0, y, 0, workspace, workspace_bytes, hip_stream);
 }

@@ -195,10 +195,34 @@ uint64_t df11_gemv_workspace_bytes(const df11_device_stream *s);
  * df11_gemv_workspace_bytes(s), 16-byte aligned, overwritten.  Each row's sum
  * is formed in a fixed order (per block, then blocks in stream order), so the
  * result is the same on every run.  Two kernels are enqueued on hip_stream.
+ * It is df11_decode_gemm with batch 1.
  * Errors: those of df11_decode, ARG for a matrix list that breaks the rules,
  * BUFSIZE for a short workspace. */
 int df11_decode_gemv(const df11_device_stream *s, const df11_gemv_matrix *mats, uint32_t n_mats,
                      const uint16_t *x, float *y, void *workspace, uint64_t workspace_bytes,
+                     void *hip_stream);
+
+#define DF11_GEMM_MAX_BATCH 8
+
+/* Bytes of device workspace df11_decode_gemm needs for s at this batch
+ * (1..8; 0 for any other batch or a null s). */
+uint64_t df11_gemm_workspace_bytes(const df11_device_stream *s, uint32_t batch);
+
+/* Fused decode and product with `batch` input vectors (1..8): for each vector
+ * b < batch and matrix m,
+ * y[b * y_stride + y_offset_m + r] = sum_c W_m[r][c] * x[b * x_stride + x_offset_m + c],
+ * with the decoded weights used for all vectors while they are on chip (the
+ * same decompress-then-matmul step as df11_decode_gemv, at small batch).
+ * Strides count elements: x_stride a multiple of 8, below 2^32 and at least
+ * the end of every matrix's inputs (max x_offset_m + cols_m); y_stride below
+ * 2^32 and at least max y_offset_m + rows_m (both ignored for batch 1).  The
+ * matrix rules, alignments, ownership, ordering and errors are those of
+ * df11_decode_gemv; the workspace must hold df11_gemm_workspace_bytes(s,
+ * batch).  Batches of 1 and 2 run at the decode's occupancy; 3 to 8 at two
+ * thirds of it. */
+int df11_decode_gemm(const df11_device_stream *s, const df11_gemv_matrix *mats, uint32_t n_mats,
+                     const uint16_t *x, uint32_t batch, uint64_t x_stride, float *y,
+                     uint64_t y_stride, void *workspace, uint64_t workspace_bytes,
                      void *hip_stream);
 
 #ifdef __cplusplus

@@ -216,6 +216,67 @@ def test_fused_gemv_llama8b_block(torch):
     _gemv_check(torch, wlx.weights, [(m.rows, m.cols) for m in wlx.matrices], "llama8b_block")
 
 
+# Fused decode + product with several input vectors: each vector's result is
+# checked like the batch-1 one, and must equal, bit for bit, what the batch-1
+# call gives for that vector alone (the same sums in the same order).
+
+def _gemm_check(torch, w, shapes, label, batch, seed=17, x_pad=24, y_pad=5):
+    enc = hd.encode(w)
+    dev = hd.to_device(enc)
+    mats, nx, ny = hd.gemv_matrices(shapes)
+    rng = np.random.default_rng(seed)
+    x_bits = wl.to_bf16(rng.standard_normal((batch, nx + x_pad)).astype(np.float32))
+    x = torch.from_numpy(x_bits.view(np.int16)).cuda().view(torch.bfloat16)
+    x_host = torch.from_numpy(x_bits.view(np.int16)).view(torch.bfloat16).float().numpy()
+    ws = torch.empty(hd.df11_gemm_workspace_bytes(dev, batch), dtype=torch.uint8, device="cuda")
+    ys = []
+    for fill in (1.0e30, -7.0):
+        y = torch.full((batch, ny + y_pad), fill, dtype=torch.float32, device="cuda")
+        _say(f"[gpu] df11_decode_gemm {label} n={enc.n} batch={batch} fill={fill}")
+        hd.df11_decode_gemm(dev, mats, x, y, ws)
+        torch.cuda.synchronize()
+        ys.append(y.cpu().numpy())
+    assert np.array_equal(ys[0][:, :ny].view(np.uint32), ys[1][:, :ny].view(np.uint32)), \
+        "not deterministic"
+    assert np.all(ys[0][:, ny:] == 1.0e30) and np.all(ys[1][:, ny:] == -7.0), "wrote past the results"
+    wf = torch.from_numpy(w.view(np.int16)).view(torch.bfloat16).float().numpy().astype(np.float64)
+    ws1 = torch.empty(hd.df11_gemv_workspace_bytes(dev), dtype=torch.uint8, device="cuda")
+    for b in range(batch):
+        off = 0
+        for m, (r, c) in zip(mats, shapes):
+            W = wf[off: off + r * c].reshape(r, c)
+            xv = x_host[b, m.x_offset: m.x_offset + c].astype(np.float64)
+            ref = W @ xv
+            bound = np.abs(W) @ np.abs(xv) * 2.0 ** -18 + 1e-30
+            got = ys[0][b, m.y_offset: m.y_offset + r].astype(np.float64)
+            bad = np.abs(got - ref) > bound
+            assert not bad.any(), (label, b, m.rows, m.cols, int(bad.sum()))
+            off += r * c
+        y1 = torch.full((ny,), 3.0, dtype=torch.float32, device="cuda")
+        hd.df11_decode_gemv(dev, mats, x[b, :nx].contiguous(), y1, ws1)
+        torch.cuda.synchronize()
+        assert np.array_equal(y1.cpu().numpy().view(np.uint32), ys[0][b, :ny].view(np.uint32)), \
+            (label, b, "differs from the batch-1 result")
+
+
+@pytest.mark.parametrize("batch", [2, 3, 5, 8])
+def test_fused_gemm_batches(torch, batch):
+    wlx = wl.llama8b_block(seed=11, scale=1 / 64)
+    _gemm_check(torch, wlx.weights, [(m.rows, m.cols) for m in wlx.matrices], "llama8b_1_64", batch)
+
+
+def test_fused_gemm_ragged_rows_and_fallback(torch):
+    wlx = wl.normal_block("r", [("a", 37, 2048), ("b", 5, 6144), ("c", 129, 2056)], 13, 0.02)
+    _gemm_check(torch, wlx.weights, [(m.rows, m.cols) for m in wlx.matrices], "ragged_rows", 4)
+    w = wl.random_small(64 * 4096, 21, "single")
+    _gemm_check(torch, w, [(64, 4096)], "single", 2)
+
+
+def test_fused_gemm_llama8b_block_batch4(torch):
+    wlx = wl.llama8b_block()
+    _gemm_check(torch, wlx.weights, [(m.rows, m.cols) for m in wlx.matrices], "llama8b_block", 4)
+
+
 def test_offload_runner_decodes_blocks_from_pinned_host_memory(torch):
     """CPU offload: blocks copied from pinned host memory per decode, two
     staging slots reused in turn; every block bit-exact."""

@@ -266,6 +266,27 @@ def test_decode_gemv_rejects_bad_matrix_lists_on_host():
     assert call(None, mats=mats) == -1                     # x slice not 8-aligned
     assert call([(1, 4096)] * 17 + [(7, 4096)]) == -1      # more than 16 matrices
 
+    # several input vectors: batch range, strides, workspace per batch capacity
+    shapes = [(24, 4096)]
+    mats = hd.gemv_matrices(shapes)[0]
+    arr = (hd.GemvMatrix * 1)(*mats)
+    for batch, floats in ((1, 4), (2, 8), (3, 16), (4, 16), (5, 28), (8, 28)):
+        assert lib.df11_gemm_workspace_bytes(ctypes.byref(d), batch) == 4 * floats * sz.n_blocks
+    assert lib.df11_gemm_workspace_bytes(ctypes.byref(d), 0) == 0
+    assert lib.df11_gemm_workspace_bytes(ctypes.byref(d), 9) == 0
+
+    def gemm(batch, xs=4096, ys=24, wsb=None):
+        wsb = lib.df11_gemm_workspace_bytes(ctypes.byref(d), batch) if wsb is None else wsb
+        return lib.df11_decode_gemm(ctypes.byref(d), arr, 1, fake, batch, xs, fake, ys, fake, wsb,
+                                    None)
+
+    assert gemm(0) == -1 and gemm(9) == -1                 # batch outside 1..8
+    assert gemm(4, xs=4100) == -1                          # x stride not a multiple of 8
+    assert gemm(4, xs=4088) == -1                          # x rows would overlap
+    assert gemm(4, ys=23) == -1                            # y rows would overlap
+    assert gemm(4, xs=1 << 32) == -1                       # stride beyond 32 bits
+    assert gemm(4, wsb=lib.df11_gemm_workspace_bytes(ctypes.byref(d), 2)) == -2  # workspace
+
 
 def test_checksum_detects_a_flipped_bit_and_offload_refuses_it():
     """One flipped stream bit desynchronises the decoder (the pages' failure
