@@ -16,7 +16,7 @@ from __future__ import annotations
 
 from dataclasses import dataclass
 
-from . import DeviceEncoded, df11_decode
+from . import DeviceEncoded, df11_decode, df11_decode_gemm, df11_gemm_workspace_bytes, gemv_matrices
 
 
 @dataclass
@@ -128,6 +128,30 @@ class StackRunner:
         s = self.compute_stream
         for i, blk in enumerate(self.blocks):
             df11_decode(blk.dev, self.buffers[i % 2], s)
+
+    def fused_inputs(self, batch: int, seed: int = 4001):
+        """Inputs and outputs for run_fused: x [batch, nx] bf16 (N(0,1) from a
+        seeded generator), y [batch, ny] fp32 and a workspace, all sized for
+        the largest block; the matrix list of every block."""
+        import torch
+        mats = [gemv_matrices(b.shapes) for b in self.blocks]
+        nx = max(m[1] for m in mats)
+        ny = max(m[2] for m in mats)
+        g = torch.Generator(device=self.device).manual_seed(seed)
+        x = torch.randn(batch, nx, generator=g, device=self.device).to(torch.bfloat16)
+        y = torch.empty(batch, ny, dtype=torch.float32, device=self.device)
+        ws = torch.empty(max(df11_gemm_workspace_bytes(b.dev, batch) for b in self.blocks),
+                         dtype=torch.uint8, device=self.device)
+        return [m[0] for m in mats], x, y, ws
+
+    def run_fused(self, mats, x, y, ws):
+        """y = W x for every block straight from its DF11 stream (no BF16
+        weights anywhere): the fused product in place of decode-then-GEMM.
+        Every block writes the same y, as a forward pass would overwrite one
+        activation buffer."""
+        s = self.compute_stream
+        for i, blk in enumerate(self.blocks):
+            df11_decode_gemm(blk.dev, mats[i], x, y, ws, s)
 
 
 class OffloadRunner:
