@@ -1,5 +1,6 @@
 // df11_decode: gfx950 (CDNA4) kernel that turns a DF11-encoded tensor back
-// into its BF16 words, and its C-ABI launcher.
+// into its BF16 words, the fused variant that multiplies the decoded weights
+// with 1-8 input vectors instead of storing them, and their C-ABI launchers.
 //
 // Page "DFloat11: lossless BFloat16 compression" (ai-infrastructure.net),
 // section "Architecture": each thread owns 8 bytes of the code stream and
@@ -18,15 +19,14 @@
 //    each entry holds the first (up to 4) codes that end inside a window
 //    narrower than the longest code -- their symbols packed in one dword,
 //    their total length and their number -- so one lookup yields up to 4
-//    exponents, stored with one 4-byte LDS store (ROCm runs gfx9 LDS in
-//    unaligned mode); codes longer than the window fall back to the 8-bit
-//    tables;
+//    exponents; codes longer than the window fall back to the 8-bit tables;
 //  * a lane's 96 relevant stream bits live in three VGPRs; windows come from
 //    one funnel shift (v_alignbit) of a dword pair, with the data pre-shifted
 //    so that the window's low bits are already the table's byte offset;
 //  * the phases are merged: phase 1 decodes each lane's codes once, into a
-//    private 40-byte staging slot in LDS, and its step count is the lane's
-//    code count.  The count is exact because the bits after the lane's last
+//    private 40-byte staging slot in LDS (the slot's partly filled dword is
+//    kept in a register, so every LDS store is an aligned two-dword store),
+//    and its step count is the lane's code count.  The count is exact because the bits after the lane's last
 //    code are forced to 1 for these lookups: all ones is a prefix of the
 //    longest code, which never completes inside the window.  After the scan
 //    each lane copies its staged exponents to its output position in the
@@ -34,7 +34,8 @@
 //    streams of 1- and 2-bit codes) send their wave down the page's own
 //    route: decode the real bits again, straight into the tile;
 //  * the merge joins 8 exponents with 8 prefetched sign|mantissa bytes per
-//    lane and writes one 16-byte store;
+//    lane and writes one 16-byte store (the fused variant instead takes the
+//    dot products of the 8 words with each input vector);
 //  * workgroups take blocks in runs of 8 from one window that moves through
 //    the whole stream, so all XCDs read and write near each other: one
 //    contiguous range per XCD put eight write fronts in step and was slower.
