@@ -151,26 +151,60 @@ __device__ __forceinline__ uint32_t lookup8(const uint16_t *lut, uint32_t w, uin
 
 __device__ __forceinline__ uint32_t leaf_len(uint32_t e) { return ((e >> 8) & 31u) + 1u; }
 
+// Workgroup barrier that orders LDS accesses only: global loads in flight
+// stay in flight across it (__syncthreads would wait for them).
+__device__ __forceinline__ void group_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Expand the 8-bit tables into the decode table (whole workgroup).  An entry
 // covers the codes that end within the first `width` bits of its index, at
 // most four: their length in bits | their number << 16, then the symbols one
 // per byte (unused bytes 0).  width = min(longest code - 1, 11): all ones is a
 // prefix of the longest code, so a run of ones never completes a code here.
 __device__ void build_decode_table(const uint16_t *lut, uint2 *dec_t, uint32_t n_tables,
-                                   uint32_t max_len) {
+                                   uint32_t max_len, uint16_t *first) {
+    // Two passes over the 2^11 windows (whole workgroup).  First the leaf of
+    // each window's first code, into `first` (scratch LDS); then an entry
+    // follows its codes through `first`: after the first code of length len,
+    // the next one is the first code of window i >> len.  Each entry thus
+    // takes single LDS reads instead of chains through the 8-bit tables, and
+    // a thread's entries are advanced side by side so their reads overlap.
+    constexpr int kPer = (1 << kDecodeBits) / kGroupThreads;
+    static_assert(kPer * kGroupThreads == (1 << kDecodeBits), "whole entries per thread");
     const uint32_t width = max_len - 1 < (uint32_t)kDecodeBits ? max_len - 1 : kDecodeBits;
-    for (int i = threadIdx.x; i < (1 << kDecodeBits); i += kGroupThreads) {
-        uint32_t pos = 0, k = 0, syms = 0;
-        while (k < (uint32_t)kMaxSymbolsPerStep) {
-            const uint32_t e = lookup8(lut, (uint32_t)i >> pos, n_tables);
-            const uint32_t len = leaf_len(e);
-            if (pos + len > width) break;
-            syms |= (e & 0xFFu) << (8 * k);
-            pos += len;
-            ++k;
-        }
-        dec_t[i] = make_uint2(pos | (k << 16), syms);
+#pragma unroll
+    for (int r = 0; r < kPer; ++r) {
+        const uint32_t i = threadIdx.x + r * kGroupThreads;
+        first[i] = (uint16_t)lookup8(lut, i, n_tables);
     }
+    group_lds_sync();
+    uint32_t pos[kPer], cnt[kPer], syms[kPer];
+    bool live[kPer];
+#pragma unroll
+    for (int r = 0; r < kPer; ++r) pos[r] = 0, cnt[r] = 0, syms[r] = 0, live[r] = true;
+#pragma unroll
+    for (int k = 0; k < kMaxSymbolsPerStep; ++k) {
+        uint32_t e[kPer];
+#pragma unroll
+        for (int r = 0; r < kPer; ++r) e[r] = first[(threadIdx.x + r * kGroupThreads) >> pos[r]];
+#pragma unroll
+        for (int r = 0; r < kPer; ++r) {
+            const uint32_t len = leaf_len(e[r]);
+            if (live[r] && pos[r] + len <= width) {
+                syms[r] |= (e[r] & 0xFFu) << (8 * k);
+                pos[r] += len;
+                ++cnt[r];
+            } else {
+                live[r] = false;
+            }
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < kPer; ++r)
+        dec_t[threadIdx.x + r * kGroupThreads] = make_uint2(pos[r] | (cnt[r] << 16), syms[r]);
 }
 
 __device__ __forceinline__ uint32_t join2(uint32_t e4, uint32_t s4, uint32_t sel_s, uint32_t sel_e) {
@@ -204,13 +238,6 @@ __device__ __forceinline__ uint32_t wave_inclusive_sum(uint32_t v) {
     return v;
 }
 
-// Workgroup barrier that orders LDS accesses only: global loads in flight
-// stay in flight across it (__syncthreads would wait for them).
-__device__ __forceinline__ void group_lds_sync() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
 
 __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -727,7 +754,8 @@ __device__ __forceinline__ void decode_blocks(const DecodeArgs &a, Sink &sink) {
         for (uint32_t i = threadIdx.x; i < lut_u4_count; i += kGroupThreads) lut_u4[i] = a.luts[i];
     }
     group_lds_sync();
-    build_decode_table(lut, dec_t, a.n_tables, a.max_len);
+    // (the wave regions are free until the block loop: scratch for the build)
+    build_decode_table(lut, dec_t, a.n_tables, a.max_len, reinterpret_cast<uint16_t *>(tiles));
     group_lds_sync();
 
     uint32_t nb = b != 0xFFFFFFFFu ? wg_block(__builtin_amdgcn_readfirstlane(claim())) : 0xFFFFFFFFu;
