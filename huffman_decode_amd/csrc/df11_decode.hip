@@ -360,14 +360,18 @@ __device__ __forceinline__ void decode_codes(const uint8_t *lds_dec, const uint1
     constexpr uint32_t kMask = ((1u << kDecodeBits) - 1) << 3;
     // pos | (LDS address of the next exponent byte) << 16; ranged: position << 16
     uint32_t acc = pos | ((kRanged ? at : tile_addr + at) << 16);
+    const uint32_t tile_end = tile_addr + kTileBytes - 4;  // last 4-byte store address
     const uint32_t stop0 = stop < 32u ? stop : 32u;
     auto step = [&](uint32_t hi, uint32_t lo, uint32_t dhi, uint32_t dlo) {
         const uint32_t w = __builtin_amdgcn_alignbit(hi, lo, acc);
         const uint2 dv = *reinterpret_cast<const uint2 *>(lds_dec + (w & kMask));
         if (!kRanged) {
             // all four symbol bytes in one (possibly unaligned) LDS store; a
-            // code longer than the table's window then overwrites byte 0
-            const uint32_t at_lds = acc >> 16;
+            // code longer than the table's window then overwrites byte 0.
+            // Valid data stays inside the block's symbols; a corrupt stream
+            // that decodes more codes here than phase 1 counted is held to
+            // the wave's region
+            const uint32_t at_lds = (acc >> 16) < tile_end ? (acc >> 16) : tile_end;
             *(lds_u32 *)(uintptr_t)at_lds = dv.y;
             uint32_t inc = dv.x;
             if (dv.x < 0x10000u) {

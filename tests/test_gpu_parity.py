@@ -109,6 +109,42 @@ def test_full_size_configs(torch, name):
         assert np.array_equal(got[p0:p1], ref), f"block {b}"
 
 
+@pytest.mark.parametrize("kind,n,seed", [("normal", 300_000, 31), ("single", 4096 * 40, 32),
+                                          ("uniform", 200_000, 33)])
+def test_flipped_stream_bits_stay_in_their_blocks(torch, kind, n, seed):
+    """A flipped stream bit desynchronises the codes of its slice (the pages'
+    failure mode).  A lane also reads 32 bits into the next slice, so a flip
+    can reach the block before its own; every other block must still decode
+    bit-exact.  A block whose code count no longer matches block_pos is
+    counted in the status word and left unwritten."""
+    import dataclasses
+    w = wl.random_small(n, seed, kind)
+    enc = hd.encode(w)
+    nb = int(enc.sizes.n_blocks)
+    rng = np.random.default_rng(seed)
+    stream = enc.stream.copy()
+    hit = set()
+    for b in sorted(set(rng.choice(nb, min(nb, 6), replace=False).tolist())):
+        bit = 4096 * b + int(rng.integers(0, 4096))
+        if bit < int(enc.sizes.total_bits):
+            stream[bit >> 3] ^= np.uint8(1 << (bit & 7))
+            hit |= {b, b - 1}
+    bad = dataclasses.replace(enc, stream=stream)
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    dev = hd.to_device(bad, status=st)
+    out = torch.full((enc.n + GUARD,), 0x5555, dtype=torch.int16, device="cuda")
+    _say(f"[gpu] df11_decode flipped bits {kind} n={enc.n} blocks={nb} hit={sorted(hit)}")
+    hd.df11_decode(dev, out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().view(np.uint16)
+    assert (got[enc.n:] == 0x5555).all(), "write past the end of the tensor"
+    bp = enc.block_pos.astype(np.int64)
+    for b in range(nb):
+        if b not in hit:
+            assert np.array_equal(got[bp[b]:bp[b + 1]], w[bp[b]:bp[b + 1]]), f"block {b}"
+    assert 0 <= int(st.item()) <= len(hit)
+
+
 def test_gemm_bit_exact_after_decode(torch):
     """The consumer GEMM sees identical weights: Y = X W^T matches bit for bit."""
     wlx = wl.linear_4096()
