@@ -24,9 +24,9 @@
 //    one funnel shift (v_alignbit) of a dword pair, with the data pre-shifted
 //    so that the window's low bits are already the table's byte offset;
 //  * the phases are merged: phase 1 decodes each lane's codes once, into a
-//    private 40-byte staging slot in LDS (the slot's partly filled dword is
-//    kept in a register, so every LDS store is an aligned two-dword store),
-//    and its step count is the lane's code count.  The count is exact because the bits after the lane's last
+//    private 40-byte staging slot in LDS (each step ORs its symbols into the
+//    slot's partly filled dword and writes the next dword, so every LDS store
+//    is aligned), and its step count is the lane's code count.  The count is exact because the bits after the lane's last
 //    code are forced to 1 for these lookups: all ones is a prefix of the
 //    longest code, which never completes inside the window.  After the scan
 //    each lane copies its staged exponents to its output position in the
@@ -259,10 +259,11 @@ __device__ __forceinline__ uint32_t pad_ones(uint32_t d, int end, int base) {
 // 1 (so a step never runs past that code and the count is exact), d* the plain
 // dwords (for codes longer than the table window).
 //
-// Stores are aligned: `cur` holds the slot's partly filled dword, and each
-// step ORs its symbols (unused table bytes are 0) in at the next byte and
-// stores the two dwords they can touch; they stay inside the wave's region
-// for any data (kStageReach).
+// Stores are aligned: each step ORs its symbols (unused table bytes are 0)
+// into the slot's partly filled dword with an LDS atomic and writes the dword
+// after it; the two dwords stay inside the wave's region for any data
+// (kStageReach).  The OR in LDS replaces a register copy of the partly filled
+// dword, which took four more VALU instructions per step.
 __device__ __forceinline__ uint32_t stage_codes(const uint8_t *lds_dec, const uint16_t *lut,
                                                 uint32_t n_tables, uint32_t d0, uint32_t d1,
                                                 uint32_t d2, uint32_t f0, uint32_t f1, uint32_t f2,
@@ -272,7 +273,12 @@ __device__ __forceinline__ uint32_t stage_codes(const uint8_t *lds_dec, const ui
                    e2 = __builtin_amdgcn_alignbit(f2, f1, 29);
     constexpr uint32_t kMask = ((1u << kDecodeBits) - 1) << 3;
     uint32_t acc = pos | (slot << 16);  // pos | (LDS address of the next byte) << 16
-    uint32_t cur = 0;                   // the dword holding that byte, bytes before it
+    // Each step ORs its symbols into the dword holding the next byte, whose
+    // bytes from that one on are 0, and writes the dword after it whole.  The
+    // symbol bytes an entry does not use are 0, so both dwords end with zeros
+    // past the last symbol: the invariant holds for the next step, and the
+    // first dword only needs clearing here.
+    *(lds_u32 *)(uintptr_t)slot = 0;
     auto step = [&](uint32_t hi, uint32_t lo, uint32_t dhi, uint32_t dlo) {
         const uint32_t w = __builtin_amdgcn_alignbit(hi, lo, acc);
         const uint2 dv = *reinterpret_cast<const uint2 *>(lds_dec + (w & kMask));
@@ -285,12 +291,10 @@ __device__ __forceinline__ uint32_t stage_codes(const uint8_t *lds_dec, const ui
         const uint32_t at = acc >> 16;
         // bits 13..17 of acc: pos >> 13 (always 0) | (byte address & 3) << 3
         const uint64_t t = (uint64_t)syms << __builtin_amdgcn_ubfe(acc, 13, 5);
-        const uint32_t w0 = cur | (uint32_t)t, w1 = (uint32_t)(t >> 32);
         lds_u32 *p = (lds_u32 *)(uintptr_t)(at & ~3u);
-        p[0] = w0;
-        p[1] = w1;
+        __atomic_fetch_or(p, (uint32_t)t, __ATOMIC_RELAXED);  // ds_or_b32, no return
+        p[1] = (uint32_t)(t >> 32);
         acc += inc;
-        cur = ((acc >> 16) ^ at) & ~3u ? w1 : w0;
     };
     // every step moves at least one bit on (table entries and 8-bit leaves
     // have lengths >= 1), so a lane takes at most 64 steps, whatever the data
