@@ -112,6 +112,7 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(1))) float g_f32;
 typedef __attribute__((address_space(1))) const u32x2 g_cu32x2;
 typedef __attribute__((address_space(1))) f32x4 g_f32x4;
+typedef __attribute__((address_space(1))) uint32_t g_u32;
 
 __device__ __forceinline__ uint32_t lds_offset(const void *p) {
     // low 32 bits of a flat address inside the LDS aperture are the LDS offset
@@ -489,6 +490,7 @@ struct GemvArgs {
     float *y;               // all matrices' results, matrix m's at y + yoff[m];
                             // vector b's at y + b * y_stride
     float *partials;        // per block: partial_floats(capacity) floats
+    uint32_t *row_blk;      // per row and one more: 2 b + (row starts after block b's start)
     uint64_t x_stride, y_stride;
     uint32_t batch;         // vectors in use, 1..capacity
     uint32_t n_mats;
@@ -550,8 +552,12 @@ struct DotSink {
     const GemvTable *tab;  // in LDS
     const g_cu16 *x;       // BF16
     g_f32x4 *partials;
+    g_u32 *row_blk;
     uint64_t x_stride;
     uint32_t batch, n_mats, lane;
+    uint32_t n, total_rows;
+    bool first_here;     // the block's first row starts at the block's first weight
+    bool last_words;     // the block holds the last weight
     uint32_t s1, s2;     // first output index of the block's second and third row
     // x index - output index: d0 in the first row, + dd1 from the second,
     // + dd2 from the third (selecting among three fields would become an
@@ -581,6 +587,8 @@ struct DotSink {
         else if (q - r * c0 >= c0) ++r;
         const uint32_t s0 = off_m + r * c0;
         grow = at(row0_l, m) + r;
+        first_here = s0 == p0;
+        last_words = p1 == n && p0 < n;
         d0 = at(xoff_l, m) - s0;
         s1 = s0 + c0;
         const uint32_t m1 = (m + 1 < n_mats && s1 >= at(off_l, m + 1)) ? m + 1 : m;
@@ -637,6 +645,14 @@ struct DotSink {
             if (b == 0 || (uint32_t)b < batch) add(pos, b, w * bf16_lo(p[b * x_stride]));
     }
     __device__ __forceinline__ void end(uint32_t blk, uint32_t) {
+        // the block of each row that starts here (the reduce's row ranges),
+        // and after the last row the block past the last weight
+        if (lane == 0) {
+            if (first_here) row_blk[grow] = 2 * blk;
+            if (row1) row_blk[grow + 1] = 2 * blk + 1;
+            if (row2) row_blk[grow + 2] = 2 * blk + 1;
+            if (last_words) row_blk[total_rows] = 2 * (blk + 1);
+        }
         // sums only for the rows the block reaches: the reduce reads a
         // block's slot for a row only if the block holds words of that row
         if constexpr (kB == 1) {
@@ -995,6 +1011,9 @@ void df11_gemm_kernel(DecodeArgs a, GemvArgs g) {
     sink.tab = &tab;
     sink.x = (const g_cu16 *)g.x;
     sink.partials = (g_f32x4 *)g.partials;
+    sink.row_blk = (g_u32 *)g.row_blk;
+    sink.n = a.n;
+    sink.total_rows = g.row0[g.n_mats];
     sink.x_stride = g.x_stride;
     sink.batch = g.batch;
     sink.n_mats = g.n_mats;
@@ -1002,69 +1021,66 @@ void df11_gemm_kernel(DecodeArgs a, GemvArgs g) {
     decode_blocks(a, sink);
 }
 
-// The last block b in [0, nb) with block_pos[b] <= v (block_pos[0] = 0 <= v):
-// galloping from a guess made from the average block size, then bisection,
-// so a thread needs a few dependent loads instead of log2(nb).
-__device__ __forceinline__ uint32_t last_block_at_or_before(const uint32_t *block_pos,
-                                                           uint32_t nb, uint32_t v) {
-    const uint32_t n = block_pos[nb];
-    uint32_t g = n ? (uint32_t)((uint64_t)v * nb / n) : 0u;
-    g = g < nb ? g : nb - 1;
-    uint32_t lo, hi;  // block_pos[lo] <= v, and hi == nb or block_pos[hi] > v
-    if (block_pos[g] <= v) {
-        lo = g;
-        uint32_t step = 1;
-        while (lo + step < nb && block_pos[lo + step] <= v) {
-            lo += step;
-            step *= 2;
-        }
-        hi = lo + step < nb ? lo + step : nb;
-    } else {
-        hi = g;
-        uint32_t step = 1;
-        while (hi >= step && block_pos[hi - step] > v) {
-            hi -= step;
-            step *= 2;
-        }
-        lo = hi >= step ? hi - step : 0u;
-    }
-    while (hi - lo > 1) {
-        const uint32_t mid = lo + (hi - lo) / 2;
-        if (block_pos[mid] <= v) lo = mid; else hi = mid;
-    }
-    return lo;
-}
-
 // y of every row and vector: the sums its blocks stored, in block order.
 template <int kB>
-__global__ __launch_bounds__(256) void df11_gemm_reduce_kernel(GemvArgs g, const uint32_t *block_pos,
-                                                               uint32_t n_blocks) {
+__global__ __launch_bounds__(256) void df11_gemm_reduce_kernel(GemvArgs g, uint32_t n_blocks) {
     const uint32_t row = blockIdx.x * 256 + threadIdx.x;
     if (row >= g.row0[g.n_mats]) return;
+    // the row's matrix and its fields, with constant indices into the
+    // kernel argument (all entries load at once; a loop would wait for each)
     uint32_t m = 0;
-    while (m + 1 < g.n_mats && row >= g.row0[m + 1]) ++m;
-    const uint32_t r = row - g.row0[m];
-    const uint32_t rs = g.off[m] + r * g.cols[m], re = rs + g.cols[m];
-    // the row's blocks: from the last one starting at or before rs to the
-    // last one starting before re (re - 1 is the row's last word); each of
-    // them holds words of the row, so its slot for the row was written
-    const uint32_t lo = last_block_at_or_before(block_pos, n_blocks, rs);
-    const uint32_t hi = last_block_at_or_before(block_pos, n_blocks, re - 1) + 1;
+#pragma unroll
+    for (int i = 1; i < kGemvMaxMats; ++i) m += (uint32_t)i < g.n_mats && row >= g.row0[i] ? 1u : 0u;
+    uint32_t row0_m = 0, yoff_m = 0;
+#pragma unroll
+    for (int i = 0; i < kGemvMaxMats; ++i)
+        if ((uint32_t)i == m) row0_m = g.row0[i], yoff_m = g.yoff[i];
+    const uint32_t r = row - row0_m;
+    // the row's blocks: from the one holding its first word to the one
+    // holding its last, which is the next row's first block, or the block
+    // before when the next row starts a block; each of them holds words of
+    // the row, so its slot for the row was written.  (The entries of rows
+    // that start in a corrupt block's place are left over from earlier
+    // calls: the range is only kept inside the workspace.)
+    const uint32_t e0 = g.row_blk[row], e1 = g.row_blk[row + 1];
+    const uint32_t lo0 = e0 >> 1, hi0 = (e1 >> 1) + (e1 & 1u);
+    const uint32_t lo = lo0 < n_blocks ? lo0 : n_blocks;
+    const uint32_t hi = hi0 < n_blocks ? hi0 : n_blocks;
     constexpr int kP = partial_floats(kB);
     float sum[kB];
 #pragma unroll
     for (int b = 0; b < kB; ++b) sum[b] = 0.0f;
-    for (uint32_t blk = lo; blk < hi; ++blk) {
-        const float *p = g.partials + (uint64_t)blk * kP;
-        const uint32_t seg = row - __float_as_uint(p[3 * kB]);  // 0, 1 or 2
-        if (seg < 3) {
+    if constexpr (kB == 1) {
+        // one vector load per record, four blocks at a time; the records stay
+        // in named registers (an array here was copied through LDS to index it)
+        auto take = [&](const f32x4 &rec, bool use) {
+            const uint32_t seg = row - __float_as_uint(rec.w);  // 0, 1 or 2
+            if (use && seg < 3) sum[0] += seg == 0 ? rec.x : seg == 1 ? rec.y : rec.z;
+        };
+        const g_f32x4 *q = (const g_f32x4 *)g.partials;
+        for (uint32_t blk = lo; blk < hi; blk += 4) {
+            const f32x4 ra = q[blk];
+            const f32x4 rb = q[blk + 1 < hi ? blk + 1 : blk];
+            const f32x4 rc = q[blk + 2 < hi ? blk + 2 : blk];
+            const f32x4 rd = q[blk + 3 < hi ? blk + 3 : blk];
+            take(ra, true);
+            take(rb, blk + 1 < hi);
+            take(rc, blk + 2 < hi);
+            take(rd, blk + 3 < hi);
+        }
+    } else {
+        for (uint32_t blk = lo; blk < hi; ++blk) {
+            const float *p = g.partials + (uint64_t)blk * kP;
+            const uint32_t seg = row - __float_as_uint(p[3 * kB]);  // 0, 1 or 2
+            if (seg < 3) {
 #pragma unroll
-            for (int b = 0; b < kB; ++b) sum[b] += p[seg * kB + b];
+                for (int b = 0; b < kB; ++b) sum[b] += p[seg * kB + b];
+            }
         }
     }
 #pragma unroll
     for (int b = 0; b < kB; ++b)
-        if ((uint32_t)b < g.batch) g.y[b * g.y_stride + g.yoff[m] + r] = sum[b];
+        if ((uint32_t)b < g.batch) g.y[b * g.y_stride + yoff_m + r] = sum[b];
 }
 
 // Launch shape per device: compute units and, per kernel, resident
@@ -1181,9 +1197,14 @@ extern "C" int df11_decode(const df11_device_stream *s, uint16_t *out, void *hip
 // batch capacity (1, 2, 4 or 8) used for a batch of 1..8 vectors
 static int gemm_capacity(uint32_t batch) { return batch <= 1 ? 1 : batch <= 2 ? 2 : batch <= 4 ? 4 : 8; }
 
+// Workspace: partial_floats(capacity) floats per block, then the row table:
+// one word per row and one more (rows have at least kGemvMinCols weights).
+static uint64_t partials_bytes(const df11_device_stream *s, uint32_t batch) {
+    return 4ull * partial_floats(gemm_capacity(batch)) * s->n_blocks;
+}
 extern "C" uint64_t df11_gemm_workspace_bytes(const df11_device_stream *s, uint32_t batch) {
     if (!s || batch < 1 || batch > (uint32_t)kGemmMaxBatch) return 0;
-    return 4ull * partial_floats(gemm_capacity(batch)) * s->n_blocks;
+    return partials_bytes(s, batch) + 4ull * (s->n / kGemvMinCols + 1);
 }
 
 extern "C" uint64_t df11_gemv_workspace_bytes(const df11_device_stream *s) {
@@ -1203,7 +1224,7 @@ static int launch_gemm(const df11_device_stream *s, const DecodeArgs &a, const G
     hipLaunchKernelGGL(df11_gemm_kernel<kB>, dim3(groups), dim3(kGroupThreads),
                        lds_bytes(s->n_tables), hs, a, g);
     hipLaunchKernelGGL(df11_gemm_reduce_kernel<kB>, dim3((uint32_t)((rows + 255) / 256)), dim3(256),
-                       0, hs, g, a.block_pos, a.n_blocks);
+                       0, hs, g, a.n_blocks);
     return hipGetLastError() == hipSuccess ? DF11_OK : DF11_ERR_HIP;
 }
 
@@ -1227,6 +1248,7 @@ extern "C" int df11_decode_gemm(const df11_device_stream *s, const df11_gemv_mat
     g.x = x;
     g.y = y;
     g.partials = static_cast<float *>(workspace);
+    g.row_blk = reinterpret_cast<uint32_t *>(static_cast<uint8_t *>(workspace) + partials_bytes(s, batch));
     g.x_stride = batch > 1 ? x_stride : 0;
     g.y_stride = batch > 1 ? y_stride : 0;
     g.batch = batch;

@@ -180,7 +180,10 @@ typedef struct df11_gemv_matrix {
 #define DF11_GEMV_MAX_MATRICES 16
 #define DF11_GEMV_MIN_COLS 2048
 
-/* Bytes of device workspace df11_decode_gemv needs for s (16 per block). */
+/* Bytes of device workspace df11_decode_gemv needs for s: 16 per block (its
+ * partial row sums), then 4 per possible row and 4 more (each row's first
+ * block; rows hold at least DF11_GEMV_MIN_COLS weights, so there are at most
+ * n / DF11_GEMV_MIN_COLS of them). */
 uint64_t df11_gemv_workspace_bytes(const df11_device_stream *s);
 
 /* Fused decode and matrix-vector product: for each matrix m,
@@ -205,7 +208,9 @@ int df11_decode_gemv(const df11_device_stream *s, const df11_gemv_matrix *mats, 
 #define DF11_GEMM_MAX_BATCH 8
 
 /* Bytes of device workspace df11_decode_gemm needs for s at this batch
- * (1..8; 0 for any other batch or a null s). */
+ * (1..8; 0 for any other batch or a null s): the partial sums of each block
+ * for the batch's capacity (1, 2, 4 or 8 vectors: 16, 32, 64 or 112 bytes),
+ * then the row table of df11_gemv_workspace_bytes. */
 uint64_t df11_gemm_workspace_bytes(const df11_device_stream *s, uint32_t batch);
 
 /* Fused decode and product with `batch` input vectors (1..8): for each vector

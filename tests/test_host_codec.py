@@ -244,8 +244,11 @@ def test_decode_gemv_rejects_bad_matrix_lists_on_host():
         sz.lut_bytes
     d.n, d.total_bits, d.last_start = sz.n, sz.total_bits, sz.last_start
     d.n_blocks, d.n_tables, d.max_len = sz.n_blocks, enc.codebook.n_tables, enc.codebook.max_len
-    assert lib.df11_gemv_workspace_bytes(ctypes.byref(d)) == 16 * sz.n_blocks
-    ws = 16 * sz.n_blocks
+    # per block 16 bytes of partial sums, then one word per possible row
+    # (rows hold at least 2048 weights) and one more
+    rows_words = 4 * (sz.n // 2048 + 1)
+    assert lib.df11_gemv_workspace_bytes(ctypes.byref(d)) == 16 * sz.n_blocks + rows_words
+    ws = 16 * sz.n_blocks + rows_words
 
     def call(shapes, x=fake, wsb=ws, mats=None):
         mats = mats if mats is not None else hd.gemv_matrices(shapes)[0]
@@ -271,7 +274,8 @@ def test_decode_gemv_rejects_bad_matrix_lists_on_host():
     mats = hd.gemv_matrices(shapes)[0]
     arr = (hd.GemvMatrix * 1)(*mats)
     for batch, floats in ((1, 4), (2, 8), (3, 16), (4, 16), (5, 28), (8, 28)):
-        assert lib.df11_gemm_workspace_bytes(ctypes.byref(d), batch) == 4 * floats * sz.n_blocks
+        assert lib.df11_gemm_workspace_bytes(ctypes.byref(d), batch) == \
+            4 * floats * sz.n_blocks + rows_words
     assert lib.df11_gemm_workspace_bytes(ctypes.byref(d), 0) == 0
     assert lib.df11_gemm_workspace_bytes(ctypes.byref(d), 9) == 0
 
