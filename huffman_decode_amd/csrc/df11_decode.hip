@@ -26,16 +26,18 @@
 //  * the phases are merged: phase 1 decodes each lane's codes once, into a
 //    private 40-byte staging slot in LDS (each step ORs its symbols into the
 //    slot's partly filled dword and writes the next dword, so every LDS store
-//    is aligned), and its step count is the lane's code count.  The count is exact because the bits after the lane's last
-//    code are forced to 1 for these lookups: all ones is a prefix of the
-//    longest code, which never completes inside the window.  After the scan
-//    each lane copies its staged exponents to its output position in the
-//    wave's tile.  Lanes with more codes than a slot holds (only near-flat
-//    streams of 1- and 2-bit codes) send their wave down the page's own
-//    route: decode the real bits again, straight into the tile;
+//    is aligned), and its step count is the lane's code count.  The count
+//    is exact because the bits after the lane's last code are forced to 1
+//    for these lookups: all ones is a prefix of the longest code, which
+//    never completes inside the window.  After the scan each lane copies
+//    its staged exponents to its output position in the wave's tile.  Lanes
+//    with more codes than a slot holds (only near-flat streams of 1- and
+//    2-bit codes) send their wave down the page's own route: decode the real
+//    bits again, straight into the tile;
 //  * the merge joins 8 exponents with 8 prefetched sign|mantissa bytes per
 //    lane and writes one 16-byte store (the fused variant instead takes the
-//    dot products of the 8 words with each input vector);
+//    dot products of the 8 words with each input vector, with a copy of the
+//    loop without row selects for blocks that lie in one row);
 //  * workgroups take blocks in runs of 8 from one window that moves through
 //    the whole stream, so all XCDs read and write near each other: one
 //    contiguous range per XCD put eight write fronts in step and was slower.
@@ -43,6 +45,7 @@
 
 #include <atomic>
 #include <cstring>
+#include <type_traits>
 
 #include "df11.h"
 #include "df11_internal.h"
@@ -460,11 +463,16 @@ struct StoreSink {  // plain decode: BF16 words to out[]
     uint16_t *out;
     struct Fetched {};
     static constexpr int kEarlyFetch = 0;
+    static constexpr bool kRowPaths = false;
+    __device__ __forceinline__ bool one_row() const { return false; }
     __device__ __forceinline__ void begin(uint32_t, uint32_t, uint32_t, uint32_t, uint32_t) {}
+    template <bool = false>
     __device__ __forceinline__ Fetched fetch(uint32_t) const { return {}; }
+    template <bool = false>
     __device__ __forceinline__ void group(uint32_t pos, uint2 e8, uint2 sm8, Fetched) {
         *reinterpret_cast<uint4 *>(out + pos) = join8(e8, sm8);
     }
+    template <bool = false>
     __device__ __forceinline__ void one(uint32_t pos, uint32_t e, uint32_t sm) {
         out[pos] = (uint16_t)join1(e, sm);
     }
@@ -549,6 +557,10 @@ struct DotSink {
     // inputs for a lane's first groups are fetched ahead of the joins only
     // while they fit the register budget
     static constexpr int kEarlyFetch = kB == 1;
+    // blocks inside one row (most of them: rows are longer than blocks)
+    // take a copy of the merge loop without the row selects
+    static constexpr bool kRowPaths = true;
+    __device__ __forceinline__ bool one_row() const { return !row1; }
     const GemvTable *tab;  // in LDS
     const g_cu16 *x;       // BF16
     g_f32x4 *partials;
@@ -603,27 +615,36 @@ struct DotSink {
 #pragma unroll
         for (int b = 0; b < kB; ++b) acc0[b] = acc1[b] = acc2[b] = 0.0f;
     }
+    template <bool kOne>
     __device__ __forceinline__ void add(uint32_t pos, int b, float v) {
-        acc0[b] += pos < s1 ? v : 0.0f;
-        acc1[b] += pos >= s1 && pos < s2 ? v : 0.0f;
-        acc2[b] += pos >= s2 ? v : 0.0f;
+        if constexpr (kOne) {
+            acc0[b] += v;
+        } else {
+            acc0[b] += pos < s1 ? v : 0.0f;
+            acc1[b] += pos >= s1 && pos < s2 ? v : 0.0f;
+            acc2[b] += pos >= s2 ? v : 0.0f;
+        }
     }
     // x index of output index pos; modular 32-bit arithmetic keeps it exact
+    template <bool kOne>
     __device__ __forceinline__ uint32_t xi(uint32_t pos) const {
+        if constexpr (kOne) return pos + d0;
         return pos + d0 + (pos >= s1 ? dd1 : 0u) + (pos >= s2 ? dd2 : 0u);
     }
     struct Fetched {
         u32x4 v[kB];  // the group's 8 BF16 inputs of each vector
     };
+    template <bool kOne = false>
     __device__ __forceinline__ Fetched fetch(uint32_t pos) const {
         Fetched f;
-        const g_cu16 *p = x + xi(pos);
+        const g_cu16 *p = x + xi<kOne>(pos);
 #pragma unroll
         for (int b = 0; b < kB; ++b)
             f.v[b] = b == 0 || (uint32_t)b < batch ? *(const g_cu32x4 *)(p + b * x_stride)
                                                   : u32x4{0, 0, 0, 0};
         return f;
     }
+    template <bool kOne = false>
     __device__ __forceinline__ void group(uint32_t pos, uint2 e8, uint2 sm8, const Fetched &f) {
         const uint4 w = join8(e8, sm8);
         // BF16 x BF16 products are exact in fp32; pairs of them are added to
@@ -634,15 +655,16 @@ struct DotSink {
             v = dot2_bf16(w.y, f.v[b].y, v);
             v = dot2_bf16(w.z, f.v[b].z, v);
             v = dot2_bf16(w.w, f.v[b].w, v);
-            add(pos, b, v);
+            add<kOne>(pos, b, v);
         }
     }
+    template <bool kOne = false>
     __device__ __forceinline__ void one(uint32_t pos, uint32_t e, uint32_t sm) {
         const float w = bf16_lo(join1(e, sm));
-        const g_cu16 *p = x + xi(pos);
+        const g_cu16 *p = x + xi<kOne>(pos);
 #pragma unroll
         for (int b = 0; b < kB; ++b)
-            if (b == 0 || (uint32_t)b < batch) add(pos, b, w * bf16_lo(p[b * x_stride]));
+            if (b == 0 || (uint32_t)b < batch) add<kOne>(pos, b, w * bf16_lo(p[b * x_stride]));
     }
     __device__ __forceinline__ void end(uint32_t blk, uint32_t) {
         // the block of each row that starts here (the reduce's row ranges),
@@ -916,41 +938,53 @@ __device__ __forceinline__ void decode_blocks(const DecodeArgs &a, Sink &sink) {
             wave_lds_sync();
         }
         if (one_pass) {
-            // ---- merge with sign|mantissa, 8 BF16 per lane per group; where
-            // the sink allows, its loads for the first rounds are issued
-            // together first (a lane without a group there fetches for group
-            // full_lo)
-            if constexpr (Sink::kEarlyFetch != 0) {
-                typename Sink::Fetched fx[kPrefetchGroups];
-                if (full_lo < full_hi) {
+            // (a sink with row paths gets the block's one-row case as its own
+            // copy of the loop: the branch is taken once per block)
+            auto tile_e8 = [&](uint32_t j) { return *reinterpret_cast<const uint2 *>(tile + 8 * j); };
+            auto merge = [&](auto one_row) {
+                constexpr bool kOne = decltype(one_row)::value;
+                // ---- merge with sign|mantissa, 8 BF16 per lane per group; where
+                // the sink allows, its loads for the first rounds are issued
+                // together first (a lane without a group there fetches for group
+                // full_lo)
+                if constexpr (Sink::kEarlyFetch != 0) {
+                    typename Sink::Fetched fx[kPrefetchGroups];
+                    if (full_lo < full_hi) {
+#pragma unroll
+                        for (int i = 0; i < kPrefetchGroups; ++i) {
+                            const uint32_t j = lane + kWave * i;
+                            const uint32_t jf = j >= full_lo && j < full_hi ? j : full_lo;
+                            fx[i] = sink.template fetch<kOne>(base + 8 * jf);
+                        }
+                    }
 #pragma unroll
                     for (int i = 0; i < kPrefetchGroups; ++i) {
                         const uint32_t j = lane + kWave * i;
-                        fx[i] = sink.fetch(base + 8 * (j >= full_lo && j < full_hi ? j : full_lo));
+                        if (j >= full_lo && j < full_hi)
+                            sink.template group<kOne>(base + 8 * j, tile_e8(j), smv[i], fx[i]);
+                    }
+                } else {
+#pragma unroll
+                    for (int i = 0; i < kPrefetchGroups; ++i) {
+                        const uint32_t j = lane + kWave * i;
+                        if (j >= full_lo && j < full_hi)
+                            sink.template group<kOne>(base + 8 * j, tile_e8(j), smv[i],
+                                                      sink.template fetch<kOne>(base + 8 * j));
                     }
                 }
-#pragma unroll
-                for (int i = 0; i < kPrefetchGroups; ++i) {
-                    const uint32_t j = lane + kWave * i;
-                    if (j >= full_lo && j < full_hi)
-                        sink.group(base + 8 * j, *reinterpret_cast<const uint2 *>(tile + 8 * j),
-                                   smv[i], fx[i]);
+                for (uint32_t j = lane + kWave * kPrefetchGroups; j < full_hi; j += kWave) {
+                    const uint2 sm = load_sm8(a.signmant + base + 8 * j);
+                    sink.template group<kOne>(base + 8 * j, tile_e8(j), sm,
+                                              sink.template fetch<kOne>(base + 8 * j));
                 }
+                if (edge) sink.template one<kOne>(edge_i, tile[edge_i - base], edge_sm);
+            };
+            if constexpr (Sink::kRowPaths) {
+                if (sink.one_row()) merge(std::integral_constant<bool, true>{});
+                else merge(std::integral_constant<bool, false>{});
             } else {
-#pragma unroll
-                for (int i = 0; i < kPrefetchGroups; ++i) {
-                    const uint32_t j = lane + kWave * i;
-                    if (j >= full_lo && j < full_hi)
-                        sink.group(base + 8 * j, *reinterpret_cast<const uint2 *>(tile + 8 * j),
-                                   smv[i], sink.fetch(base + 8 * j));
-                }
+                merge(std::integral_constant<bool, false>{});
             }
-            for (uint32_t j = lane + kWave * kPrefetchGroups; j < full_hi; j += kWave) {
-                const uint2 sm = load_sm8(a.signmant + base + 8 * j);
-                sink.group(base + 8 * j, *reinterpret_cast<const uint2 *>(tile + 8 * j), sm,
-                           sink.fetch(base + 8 * j));
-            }
-            if (edge) sink.one(edge_i, tile[edge_i - base], edge_sm);
             wave_lds_sync();
         } else {
             // more symbols than one tile holds: decode again per tile-sized window
