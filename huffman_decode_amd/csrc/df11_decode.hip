@@ -937,9 +937,12 @@ __device__ __forceinline__ void decode_blocks(const DecodeArgs &a, Sink &sink) {
             rewrite_head(lds_dec, lut, a.n_tables, d0, d1, d2, start, cnt, tile_addr + at);
             wave_lds_sync();
         }
-        if (one_pass) {
-            // (a sink with row paths gets the block's one-row case as its own
-            // copy of the loop: the branch is taken once per block)
+        if (one_pass && Sink::kRowPaths) {
+            // a sink with row paths gets the block's one-row case as its own
+            // copy of the loop: the branch is taken once per block.  (The
+            // plain decode keeps the single loop below: the same code shape
+            // for it measured 26% slower, from scheduling alone.)
+            if constexpr (Sink::kRowPaths) {
             auto tile_e8 = [&](uint32_t j) { return *reinterpret_cast<const uint2 *>(tile + 8 * j); };
             auto merge = [&](auto one_row) {
                 constexpr bool kOne = decltype(one_row)::value;
@@ -979,12 +982,46 @@ __device__ __forceinline__ void decode_blocks(const DecodeArgs &a, Sink &sink) {
                 }
                 if (edge) sink.template one<kOne>(edge_i, tile[edge_i - base], edge_sm);
             };
-            if constexpr (Sink::kRowPaths) {
-                if (sink.one_row()) merge(std::integral_constant<bool, true>{});
-                else merge(std::integral_constant<bool, false>{});
-            } else {
-                merge(std::integral_constant<bool, false>{});
+            if (sink.one_row()) merge(std::integral_constant<bool, true>{});
+            else merge(std::integral_constant<bool, false>{});
+            wave_lds_sync();
             }
+        } else if (one_pass) {
+            // ---- merge with sign|mantissa, 8 BF16 per lane per group; where
+            // the sink allows, its loads for the first rounds are issued
+            // together first (a lane without a group there fetches for group
+            // full_lo)
+            if constexpr (Sink::kEarlyFetch != 0) {
+                typename Sink::Fetched fx[kPrefetchGroups];
+                if (full_lo < full_hi) {
+#pragma unroll
+                    for (int i = 0; i < kPrefetchGroups; ++i) {
+                        const uint32_t j = lane + kWave * i;
+                        fx[i] = sink.fetch(base + 8 * (j >= full_lo && j < full_hi ? j : full_lo));
+                    }
+                }
+#pragma unroll
+                for (int i = 0; i < kPrefetchGroups; ++i) {
+                    const uint32_t j = lane + kWave * i;
+                    if (j >= full_lo && j < full_hi)
+                        sink.group(base + 8 * j, *reinterpret_cast<const uint2 *>(tile + 8 * j),
+                                   smv[i], fx[i]);
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < kPrefetchGroups; ++i) {
+                    const uint32_t j = lane + kWave * i;
+                    if (j >= full_lo && j < full_hi)
+                        sink.group(base + 8 * j, *reinterpret_cast<const uint2 *>(tile + 8 * j),
+                                   smv[i], sink.fetch(base + 8 * j));
+                }
+            }
+            for (uint32_t j = lane + kWave * kPrefetchGroups; j < full_hi; j += kWave) {
+                const uint2 sm = load_sm8(a.signmant + base + 8 * j);
+                sink.group(base + 8 * j, *reinterpret_cast<const uint2 *>(tile + 8 * j), sm,
+                           sink.fetch(base + 8 * j));
+            }
+            if (edge) sink.one(edge_i, tile[edge_i - base], edge_sm);
             wave_lds_sync();
         } else {
             // more symbols than one tile holds: decode again per tile-sized window
@@ -1101,6 +1138,38 @@ __global__ __launch_bounds__(256) void df11_gemm_reduce_kernel(GemvArgs g, uint3
             take(rb, blk + 1 < hi);
             take(rc, blk + 2 < hi);
             take(rd, blk + 3 < hi);
+        }
+    } else if constexpr (kB <= 4) {
+        // whole records (16-byte loads), two blocks at a time; each loaded
+        // word is pinned to a register so that the segment select stays a
+        // select between registers (for 8 vectors the records are too large
+        // for this to pay: measured slower)
+        constexpr int kV = kP / 4;
+        const g_f32x4 *q = (const g_f32x4 *)g.partials;
+        for (uint32_t blk = lo; blk < hi; blk += 2) {
+            const uint32_t bb = blk + 1 < hi ? blk + 1 : blk;
+            f32x4 ra[kV], rb[kV];
+#pragma unroll
+            for (int v = 0; v < kV; ++v) {
+                ra[v] = q[(uint64_t)blk * kV + v];
+                rb[v] = q[(uint64_t)bb * kV + v];
+            }
+#pragma unroll
+            for (int v = 0; v < kV; ++v) asm volatile("" : "+v"(ra[v]), "+v"(rb[v]));
+            auto take = [&](const f32x4 (&r)[kV], bool use) {
+                const uint32_t seg = row - __float_as_uint(r[(3 * kB) / 4][(3 * kB) % 4]);
+                if (use && seg < 3) {
+#pragma unroll
+                    for (int b = 0; b < kB; ++b) {
+                        const float v0 = r[b / 4][b % 4];
+                        const float v1 = r[(kB + b) / 4][(kB + b) % 4];
+                        const float v2 = r[(2 * kB + b) / 4][(2 * kB + b) % 4];
+                        sum[b] += seg == 0 ? v0 : seg == 1 ? v1 : v2;
+                    }
+                }
+            };
+            take(ra, true);
+            take(rb, blk + 1 < hi);
         }
     } else {
         for (uint32_t blk = lo; blk < hi; ++blk) {
