@@ -145,6 +145,103 @@ def test_flipped_stream_bits_stay_in_their_blocks(torch, kind, n, seed):
     assert 0 <= int(st.item()) <= len(hit)
 
 
+def _corrupt(enc, seed, n_flips=3, bad_pos=True):
+    """Flip stream bits in a few blocks and, optionally, overwrite one interior
+    block_pos entry with a position past the end.  Returns the corrupted
+    arrays and the blocks whose output may be wrong: a flip reaches its own
+    block and the one before (a lane reads 32 bits into the next slice), and a
+    bad entry makes both blocks that share it fail the host's range check."""
+    import dataclasses
+    nb = int(enc.sizes.n_blocks)
+    rng = np.random.default_rng(seed)
+    stream = enc.stream.copy()
+    hit = set()
+    for b in sorted(set(rng.choice(nb, min(nb, n_flips), replace=False).tolist())):
+        bit = 4096 * b + int(rng.integers(0, 4096))
+        if bit < int(enc.sizes.total_bits):
+            stream[bit >> 3] ^= np.uint8(1 << (bit & 7))
+            hit |= {b, b - 1}
+    block_pos = enc.block_pos.copy()
+    if bad_pos and nb > 4:
+        b = int(rng.integers(2, nb - 1))
+        block_pos[b] = np.uint32(enc.n + 12345)
+        hit |= {b - 1, b}
+    return dataclasses.replace(enc, stream=stream, block_pos=block_pos), hit
+
+
+@pytest.mark.parametrize("seed", [11, 12])
+def test_corrupt_block_pos_leaves_other_blocks_exact(torch, seed):
+    """A block_pos entry past the end fails the range check of the two blocks
+    that share it: both are counted and left unwritten, with no access outside
+    the arrays, and every other block (flipped stream bits aside) decodes
+    bit-exact."""
+    w = wl.random_small(40 * 4096, seed, "normal")
+    enc = hd.encode(w)
+    bad, hit = _corrupt(enc, seed)
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    dev = hd.to_device(bad, status=st)
+    out = torch.full((enc.n + GUARD,), 0x5555, dtype=torch.int16, device="cuda")
+    _say(f"[gpu] df11_decode corrupt block_pos seed={seed} hit={sorted(hit)}")
+    hd.df11_decode(dev, out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().view(np.uint16)
+    assert (got[enc.n:] == 0x5555).all(), "write past the end of the tensor"
+    bp = enc.block_pos.astype(np.int64)
+    for b in range(int(enc.sizes.n_blocks)):
+        if b not in hit:
+            assert np.array_equal(got[bp[b]:bp[b + 1]], w[bp[b]:bp[b + 1]]), f"block {b}"
+    assert 2 <= int(st.item()) <= len(hit)
+
+
+def test_fused_gemv_with_corrupt_blocks(torch):
+    """The fused product on a corrupted stream: blocks that fail their checks
+    leave stale partial sums and row-table entries in a workspace full of
+    garbage; the reduce keeps every read inside the workspace, and each row
+    whose words all lie in intact blocks still gets its exact-within-bound
+    sum."""
+    shapes = [(24, 4096), (8, 8192)]
+    n = sum(r * c for r, c in shapes)
+    w = wl.random_small(n, 21, "normal")
+    enc = hd.encode(w)
+    bad, hit = _corrupt(enc, 21)
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    dev = hd.to_device(bad, status=st)
+    mats, nx, ny = hd.gemv_matrices(shapes)
+    rng = np.random.default_rng(22)
+    x_bits = wl.to_bf16(rng.standard_normal(nx).astype(np.float32))
+    x = torch.from_numpy(x_bits.view(np.int16)).cuda().view(torch.bfloat16)
+    ws = torch.full((hd.df11_gemv_workspace_bytes(dev),), 0xFF, dtype=torch.uint8, device="cuda")
+    y = torch.full((ny + 5,), 2.5, dtype=torch.float32, device="cuda")
+    _say(f"[gpu] df11_decode_gemv corrupt blocks hit={sorted(hit)}")
+    hd.df11_decode_gemv(dev, mats, x, y, ws)
+    torch.cuda.synchronize()
+    got = y.cpu().numpy().astype(np.float64)
+    assert np.all(got[ny:] == 2.5), "wrote past the results"
+    assert int(st.item()) >= 2
+    bp = enc.block_pos.astype(np.int64)
+    block_of = lambda pos: int(np.searchsorted(bp, pos, side="right") - 1)
+    xv_all = torch.from_numpy(x_bits.view(np.int16)).view(torch.bfloat16).float().numpy()
+    wf = torch.from_numpy(w.view(np.int16)).view(torch.bfloat16).float().numpy().astype(np.float64)
+    off, checked = 0, 0
+    for m, (r, c) in zip(mats, shapes):
+        for row in range(r):
+            rs, re = off + row * c, off + (row + 1) * c
+            touched = set(range(block_of(rs), block_of(re - 1) + 1))
+            # the row's range also comes from the next row's table entry
+            if re < n:
+                touched.add(block_of(re))
+            if touched & hit:
+                continue
+            W = wf[rs:re]
+            xv = xv_all[m.x_offset: m.x_offset + c].astype(np.float64)
+            ref = W @ xv
+            bound = np.abs(W) @ np.abs(xv) * 2.0 ** -18 + 1e-30
+            assert abs(got[m.y_offset + row] - ref) <= bound, (m.rows, row)
+            checked += 1
+        off += r * c
+    assert checked > 0
+
+
 def test_gemm_bit_exact_after_decode(torch):
     """The consumer GEMM sees identical weights: Y = X W^T matches bit for bit."""
     wlx = wl.linear_4096()
