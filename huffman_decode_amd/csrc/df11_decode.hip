@@ -14,8 +14,9 @@
 // Mapping onto CDNA4 (the decoder is integer VALU + LDS work; no MFMA):
 //  * a format block (64 slices, 512 stream bytes) is one wave64, so the prefix
 //    sum is a wave-level scan and no workgroup barrier sits in the block loop;
-//  * workgroups are persistent; each stages the 8-bit tables and expands them
-//    in LDS into a multi-code decode table indexed by the next 11 stream bits:
+//  * workgroups are persistent; each stages in LDS the 8-bit tables and the
+//    multi-code decode table that the host library appends to them (built
+//    once per codebook), indexed by the next 11 stream bits:
 //    each entry holds the first (up to 4) codes that end inside a window
 //    narrower than the longest code -- their symbols packed in one dword,
 //    their total length and their number -- so one lookup yields up to 4
@@ -55,9 +56,6 @@ namespace {
 #ifndef DF11_WAVES_PER_GROUP
 #define DF11_WAVES_PER_GROUP 8
 #endif
-#ifndef DF11_DECODE_BITS
-#define DF11_DECODE_BITS 11
-#endif
 
 constexpr int kWave = 64;
 constexpr int kWavesPerGroup = DF11_WAVES_PER_GROUP;
@@ -86,9 +84,10 @@ static_assert(kStageStride % 4 == 0 && kStageBase % 4 == 0 && kTileBytes % 8 == 
 static_assert(kStageStride >= kStageCodes + 4, "a full slot takes 4 stray bytes");
 constexpr int kTableBytes = 256 * 2;
 constexpr int kXcds = 8;
-// multi-code decode table (LDS): index width
-constexpr int kDecodeBits = DF11_DECODE_BITS;
-constexpr int kDecodeBytes = (1 << kDecodeBits) * 8;
+// multi-code decode table (built by the host after the 8-bit tables of the
+// table image, copied to LDS by each workgroup): index width
+constexpr int kDecodeBits = (int)df11_internal::kDecodeTableBits;
+constexpr int kDecodeBytes = (int)df11_internal::kDecodeTableBytes;
 constexpr int kMaxSymbolsPerStep = 4;
 constexpr int kTilesBytes = kWavesPerGroup * kTileBytes;
 constexpr int kStaticLds = kTilesBytes + kDecodeBytes;
@@ -161,54 +160,6 @@ __device__ __forceinline__ void group_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
-// Expand the 8-bit tables into the decode table (whole workgroup).  An entry
-// covers the codes that end within the first `width` bits of its index, at
-// most four: their length in bits | their number << 16, then the symbols one
-// per byte (unused bytes 0).  width = min(longest code - 1, 11): all ones is a
-// prefix of the longest code, so a run of ones never completes a code here.
-__device__ void build_decode_table(const uint16_t *lut, uint2 *dec_t, uint32_t n_tables,
-                                   uint32_t max_len, uint16_t *first) {
-    // Two passes over the 2^11 windows (whole workgroup).  First the leaf of
-    // each window's first code, into `first` (scratch LDS); then an entry
-    // follows its codes through `first`: after the first code of length len,
-    // the next one is the first code of window i >> len.  Each entry thus
-    // takes single LDS reads instead of chains through the 8-bit tables, and
-    // a thread's entries are advanced side by side so their reads overlap.
-    constexpr int kPer = (1 << kDecodeBits) / kGroupThreads;
-    static_assert(kPer * kGroupThreads == (1 << kDecodeBits), "whole entries per thread");
-    const uint32_t width = max_len - 1 < (uint32_t)kDecodeBits ? max_len - 1 : kDecodeBits;
-#pragma unroll
-    for (int r = 0; r < kPer; ++r) {
-        const uint32_t i = threadIdx.x + r * kGroupThreads;
-        first[i] = (uint16_t)lookup8(lut, i, n_tables);
-    }
-    group_lds_sync();
-    uint32_t pos[kPer], cnt[kPer], syms[kPer];
-    bool live[kPer];
-#pragma unroll
-    for (int r = 0; r < kPer; ++r) pos[r] = 0, cnt[r] = 0, syms[r] = 0, live[r] = true;
-#pragma unroll
-    for (int k = 0; k < kMaxSymbolsPerStep; ++k) {
-        uint32_t e[kPer];
-#pragma unroll
-        for (int r = 0; r < kPer; ++r) e[r] = first[(threadIdx.x + r * kGroupThreads) >> pos[r]];
-#pragma unroll
-        for (int r = 0; r < kPer; ++r) {
-            const uint32_t len = leaf_len(e[r]);
-            if (live[r] && pos[r] + len <= width) {
-                syms[r] |= (e[r] & 0xFFu) << (8 * k);
-                pos[r] += len;
-                ++cnt[r];
-            } else {
-                live[r] = false;
-            }
-        }
-    }
-#pragma unroll
-    for (int r = 0; r < kPer; ++r)
-        dec_t[threadIdx.x + r * kGroupThreads] = make_uint2(pos[r] | (cnt[r] << 16), syms[r]);
 }
 
 __device__ __forceinline__ uint32_t join2(uint32_t e4, uint32_t s4, uint32_t sel_s, uint32_t sel_e) {
@@ -770,15 +721,19 @@ __device__ __forceinline__ void decode_blocks(const DecodeArgs &a, Sink &sink) {
         if (lane == 0) v = atomicAdd(&wg_next, 1u);
         return v;
     };
-    // The 8-bit tables' load goes first (up to 16 tables, one 16-B load per
-    // thread; more tables are loaded below), then each wave's first block:
-    // wave w takes the workgroup's claim w without the counter, so that its
-    // loads are in flight while the tables are staged and the decode table is
-    // built.
+    // The tables' loads go first (the 8-bit tables, up to 16 of them in one
+    // 16-B load per thread, more below; then the decode table), then each
+    // wave's first block: wave w takes the workgroup's claim w without the
+    // counter, so that its loads are in flight while the tables are staged.
     const uint32_t lut_u4_count = hier_bytes / 16;
     const bool lut_one_load = lut_u4_count <= kGroupThreads;
     uint4 lv = {0, 0, 0, 0};
     if (lut_one_load && threadIdx.x < lut_u4_count) lv = a.luts[threadIdx.x];
+    // the decode table follows the 8-bit tables in the image: two 16-byte
+    // loads per thread
+    static_assert(kDecodeBytes == 2 * 16 * kGroupThreads, "two uint4 per thread");
+    const uint4 *dec_src = a.luts + lut_u4_count;
+    const uint4 dv0 = dec_src[threadIdx.x], dv1 = dec_src[threadIdx.x + kGroupThreads];
     uint32_t b = wg_block(wave);
     uint32_t nd0, nd1, nd2, ng0, ng1, npos;
     {
@@ -799,9 +754,8 @@ __device__ __forceinline__ void decode_blocks(const DecodeArgs &a, Sink &sink) {
     } else {
         for (uint32_t i = threadIdx.x; i < lut_u4_count; i += kGroupThreads) lut_u4[i] = a.luts[i];
     }
-    group_lds_sync();
-    // (the wave regions are free until the block loop: scratch for the build)
-    build_decode_table(lut, dec_t, a.n_tables, a.max_len, reinterpret_cast<uint16_t *>(tiles));
+    reinterpret_cast<uint4 *>(dec_t)[threadIdx.x] = dv0;
+    reinterpret_cast<uint4 *>(dec_t)[threadIdx.x + kGroupThreads] = dv1;
     group_lds_sync();
 
     uint32_t nb = b != 0xFFFFFFFFu ? wg_block(__builtin_amdgcn_readfirstlane(claim())) : 0xFFFFFFFFu;

@@ -191,14 +191,63 @@ int count_tables(const uint8_t *len, const uint32_t *code) {
     return tables;
 }
 
-uint64_t lut_image_bytes(uint32_t n_tables) { return (uint64_t)n_tables * 256 * 2; }
+uint64_t lut_image_bytes(uint32_t n_tables) {
+    return (uint64_t)n_tables * 256 * 2 + kDecodeTableBytes;
+}
 
 }  // namespace df11_internal
 
+namespace {
+
+using df11_internal::kDecodeTableBits;
+using df11_internal::kDecodeTableEntries;
+
+// The leaf the 8-bit tables give for stream window w (first bit in bit 0),
+// following at most three pointers; a pointer to a table past n_tables goes
+// to table 0, and a pointer left after the last hop reads as a leaf.
+uint32_t table_leaf(const uint16_t *lut, uint32_t w, uint32_t n_tables) {
+    uint32_t e = lut[w & 0xFFu];
+    for (int lvl = 1; lvl < 4 && (e & 0x8000u); ++lvl) {
+        const uint32_t t = (e & 63u) < n_tables ? (e & 63u) : 0u;
+        e = lut[t * 256u + ((w >> (8 * lvl)) & 0xFFu)];
+    }
+    return e;
+}
+
+// The multi-code decode table for the kernel.  Entry i covers the codes at
+// the start of window i that end within its first width = min(max_len - 1,
+// kDecodeTableBits) bits, at most four.  It stores their total length |
+// their number << 16, then their symbols one per byte (unused bytes 0).
+// All ones is a prefix of the longest code, so a window of ones never
+// completes one here.  A code longer than the window leaves the entry empty,
+// and the kernel resolves it through the 8-bit tables.  The next code of
+// window i is the first code of window i >> length.
+void build_decode_table(const uint16_t *lut, uint32_t n_tables, uint32_t max_len, uint32_t *out) {
+    const uint32_t width = max_len - 1 < kDecodeTableBits ? max_len - 1 : kDecodeTableBits;
+    std::vector<uint32_t> first(kDecodeTableEntries);
+    for (uint32_t i = 0; i < kDecodeTableEntries; ++i) first[i] = table_leaf(lut, i, n_tables);
+    for (uint32_t i = 0; i < kDecodeTableEntries; ++i) {
+        uint32_t pos = 0, cnt = 0, syms = 0;
+        for (uint32_t k = 0; k < 4; ++k) {
+            const uint32_t e = first[i >> pos];
+            const uint32_t len = ((e >> 8) & 31u) + 1;
+            if (pos + len > width) break;
+            syms |= (e & 0xFFu) << (8 * k);
+            pos += len;
+            ++cnt;
+        }
+        out[2 * i] = pos | (cnt << 16);
+        out[2 * i + 1] = syms;
+    }
+}
+
+}  // namespace
+
 // Device table image: n_tables tables of 256 uint16 entries, indexed by the
-// next 8 stream bits with the first stream bit in bit 0 of the index.
+// next 8 stream bits with the first stream bit in bit 0 of the index,
 //   leaf    : bits 0-7 symbol, bits 8-12 (total code length - 1), bit 15 = 0
-//   pointer : bit 15 = 1, bits 0-5 child table (the next 8 bits index it)
+//   pointer : bit 15 = 1, bits 0-5 child table (the next 8 bits index it),
+// then the multi-code decode table (build_decode_table above).
 // Unreachable entries (only the one-symbol code has any) are leaves of
 // symbol 0, length 1, so a decoder always advances.
 extern "C" int df11_build_luts(const df11_codebook *cb, void *lut, uint64_t lut_cap) {
@@ -238,6 +287,9 @@ extern "C" int df11_build_luts(const df11_codebook *cb, void *lut, uint64_t lut_
         const uint16_t leaf = (uint16_t)((unsigned)s | ((L - 1) << 8));
         for (uint32_t hi = 0; hi < (1u << (8 - rest)); ++hi) t[tab * 256 + (low | (hi << rest))] = leaf;
     }
+    // the decode table follows the 8-bit tables (16-byte aligned: n_tables x 512 bytes)
+    build_decode_table(t, cb->n_tables, cb->max_len,
+                       reinterpret_cast<uint32_t *>(t + cb->n_tables * 256));
     return DF11_OK;
 }
 

@@ -98,8 +98,10 @@ typedef struct df11_codebook {
  * Errors: ARG (null, empty histogram), CODELEN, TABLES. */
 int df11_build_codebook(const uint64_t hist[256], uint32_t max_code_len, df11_codebook *cb);
 
-/* Device table image (cb->lut_bytes bytes) into lut.  Section
- * "Architecture", hierarchical lookup tables.  Errors: ARG, BUFSIZE. */
+/* Device table image (cb->lut_bytes bytes) into lut: the hierarchical 8-bit
+ * lookup tables of section "Architecture", then a multi-code decode table
+ * derived from them, which the kernel copies to LDS as it is (both follow
+ * from code_len[] alone).  Errors: ARG, BUFSIZE. */
 int df11_build_luts(const df11_codebook *cb, void *lut, uint64_t lut_cap);
 
 /* Sizes of every encoded array for n weights with histogram hist. */

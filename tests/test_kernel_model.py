@@ -219,3 +219,25 @@ def test_model_longest_codes():
     starts = np.concatenate([[0], np.cumsum(ln[e].astype(np.int64))])
     idx = np.nonzero(ln[e] >= 30)[0][:3]
     _check(w, blocks=sorted({int(starts[i]) // 4096 for i in idx}))
+
+
+@pytest.mark.parametrize("kind", ["normal", "uniform", "single", "fibonacci_33"])
+def test_host_decode_table_matches_model(kind):
+    """The table image ends with the multi-code decode table that the kernel
+    copies to LDS (built by the host library).  Every entry must be the
+    model's: total length | code count << 16, then the symbols, unused bytes 0.
+    The cases cover short codes, a flat code, the one-symbol code (no code
+    fits the window, every entry is empty) and codes up to 32 bits."""
+    if kind == "fibonacci_33":
+        w = wl.fibonacci_exponents(33, 5002, 1024, 16384).weights
+    else:
+        w = wl.random_small({"normal": 100_000, "uniform": 50_000, "single": 4096}[kind], 3, kind)
+    enc = hd.encode(w)
+    n_tables = enc.codebook.n_tables
+    lut = enc.luts.view(np.uint16)
+    tail = enc.luts[n_tables * 512:].view(np.uint32)
+    assert tail.size == 2 * (1 << DECODE_BITS)
+    for i, (pos, k, syms) in enumerate(_table(lut, n_tables, enc.codebook.max_len)):
+        packed = sum(int(s) << (8 * j) for j, s in enumerate(syms[:k]))
+        assert int(tail[2 * i]) == pos | (k << 16), (kind, i)
+        assert int(tail[2 * i + 1]) == packed, (kind, i)
