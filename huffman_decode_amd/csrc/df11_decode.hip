@@ -135,7 +135,6 @@ struct DecodeArgs {
     uint32_t stop_blk, stop_rem, end_blk, end_rem;
     uint32_t n_blocks;
     uint32_t n_tables;
-    uint32_t max_len;
 };
 
 // 8-bit table entry: leaf = symbol | (length - 1) << 8; pointer = 0x8000 |
@@ -1230,7 +1229,6 @@ int prepare(const df11_device_stream *s, uint16_t *out, DecodeArgs *a) {
     a->end_rem = (uint32_t)(s->total_bits & 4095);
     a->n_blocks = s->n_blocks;
     a->n_tables = s->n_tables;
-    a->max_len = s->max_len;
     return DF11_OK;
 }
 
