@@ -57,7 +57,8 @@ def algorithmic_bytes(enc) -> tuple[int, int]:
 
 def measured_traffic(n_launch_bytes: int):
     """HBM bytes per launch from committed rocprofv3 counters, if they were taken
-    on the current kernel source; else None."""
+    on the current kernel source and on this workload (the profile's
+    algorithmic bytes per launch equal n_launch_bytes); else None."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     vals = {}
@@ -69,6 +70,8 @@ def measured_traffic(n_launch_bytes: int):
     if vals.get("kernel_sha256_16") != kernel_hash():
         return None
     try:
+        if int(vals["algorithmic_bytes_per_launch"]) != int(n_launch_bytes):
+            return None
         return int(float(vals["hbm_bytes_per_launch"]))
     except (KeyError, ValueError):
         return None

@@ -310,3 +310,22 @@ def test_checksum_detects_a_flipped_bit_and_offload_refuses_it():
     enc.stream[100] ^= 1
     with pytest.raises(ValueError, match="checksum mismatch"):
         OffloadRunner([enc], [good])
+
+
+def test_bench_reports_traffic_only_for_the_profiled_workload():
+    """bench.py takes roofline.traffic from the committed counter profile only
+    when that profile was taken on the current kernel source and on the
+    workload being measured (same algorithmic bytes per launch)."""
+    import importlib.util
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    spec = importlib.util.spec_from_file_location("bench_mod", os.path.join(root, "bench.py"))
+    bench = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(bench)
+    text = open(bench.TRAFFIC_FILE).read()
+    alg = int(re.search(r"^algorithmic_bytes_per_launch: (\d+)", text, re.M).group(1))
+    assert bench.measured_traffic(alg + 1) is None
+    got = bench.measured_traffic(alg)
+    if re.search(r"^kernel_sha256_16: (\w+)", text, re.M).group(1) == bench.kernel_hash():
+        assert got is not None and 0.95 * alg < got < 1.10 * alg
+    else:
+        assert got is None
