@@ -504,8 +504,8 @@ struct GemvTable {
 
 template <int kB>
 struct DotSink {
-    // inputs for a lane's first groups are fetched ahead of the joins only
-    // while they fit the register budget
+    // inputs of a lane's first groups are fetched at the block's top, before
+    // phase 1, only while they fit the register budget (one vector: 79 VGPRs)
     static constexpr int kEarlyFetch = kB == 1;
     // blocks inside one row (most of them: rows are longer than blocks)
     // take a copy of the merge loop without the row selects
@@ -810,6 +810,23 @@ __device__ __forceinline__ void decode_blocks(const DecodeArgs &a, Sink &sink) {
                          : make_uint2(0, 0);
         }
 
+        // a sink that fetches inputs: its block set-up and the inputs of the
+        // lane's first groups go out here, so that their latency passes
+        // during phase 1 (a lane without a group there fetches for full_lo)
+        typename Sink::Fetched fx0[kPrefetchGroups];
+        if constexpr (Sink::kEarlyFetch != 0) {
+            if (sane) {
+                sink.begin(p0, p1, base, 0, 0);
+                if (one_pass && full_lo < full_hi) {
+#pragma unroll
+                    for (int i = 0; i < kPrefetchGroups; ++i) {
+                        const uint32_t j = lane + kWave * i;
+                        const uint32_t jf = j >= full_lo && j < full_hi ? j : full_lo;
+                        fx0[i] = sink.fetch(base + 8 * jf);
+                    }
+                }
+            }
+        }
         const uint32_t gw = __builtin_amdgcn_alignbit(gw1, gw0, gap_shift);
         const uint32_t gap = gw & 31u, gap_next = (gw >> 5) & 31u;
         // the stop bit and the stream end relative to this lane's slice:
@@ -859,12 +876,13 @@ __device__ __forceinline__ void decode_blocks(const DecodeArgs &a, Sink &sink) {
         if (!sane || total != p1 - p0) {
             if (lane == 0 && a.status) atomicAdd(a.status, 1u);
             if (sane) {  // leave a defined (empty) result for the block
-                sink.begin(p0, p1, base, 0, 0);
+                if constexpr (Sink::kEarlyFetch == 0) sink.begin(p0, p1, base, 0, 0);
                 sink.end(cur_blk, lane);
             }
             continue;
         }
-        sink.begin(p0, p1, base, one_pass ? full_lo : 0u, one_pass ? full_hi : 0u);
+        if constexpr (Sink::kEarlyFetch == 0)  // (a fetching sink began at the block's top)
+            sink.begin(p0, p1, base, one_pass ? full_lo : 0u, one_pass ? full_hi : 0u);
         const uint32_t at = (p0 - base) + excl;  // tile position of this lane's first symbol
         const uint32_t stop = lim ? lim : 0u;
         const uint32_t start = lim ? gap : 0u;
@@ -904,15 +922,7 @@ __device__ __forceinline__ void decode_blocks(const DecodeArgs &a, Sink &sink) {
                 // together first (a lane without a group there fetches for group
                 // full_lo)
                 if constexpr (Sink::kEarlyFetch != 0) {
-                    typename Sink::Fetched fx[kPrefetchGroups];
-                    if (full_lo < full_hi) {
-#pragma unroll
-                        for (int i = 0; i < kPrefetchGroups; ++i) {
-                            const uint32_t j = lane + kWave * i;
-                            const uint32_t jf = j >= full_lo && j < full_hi ? j : full_lo;
-                            fx[i] = sink.template fetch<kOne>(base + 8 * jf);
-                        }
-                    }
+                    const typename Sink::Fetched *fx = fx0;  // fetched at the block's top
 #pragma unroll
                     for (int i = 0; i < kPrefetchGroups; ++i) {
                         const uint32_t j = lane + kWave * i;
@@ -940,34 +950,15 @@ __device__ __forceinline__ void decode_blocks(const DecodeArgs &a, Sink &sink) {
             wave_lds_sync();
             }
         } else if (one_pass) {
-            // ---- merge with sign|mantissa, 8 BF16 per lane per group; where
-            // the sink allows, its loads for the first rounds are issued
-            // together first (a lane without a group there fetches for group
-            // full_lo)
-            if constexpr (Sink::kEarlyFetch != 0) {
-                typename Sink::Fetched fx[kPrefetchGroups];
-                if (full_lo < full_hi) {
+            // ---- merge with sign|mantissa, 8 BF16 per lane per group (a sink
+            // without row paths fetches nothing ahead)
+            static_assert(Sink::kRowPaths || Sink::kEarlyFetch == 0, "early fetches need the row-path loop");
 #pragma unroll
-                    for (int i = 0; i < kPrefetchGroups; ++i) {
-                        const uint32_t j = lane + kWave * i;
-                        fx[i] = sink.fetch(base + 8 * (j >= full_lo && j < full_hi ? j : full_lo));
-                    }
-                }
-#pragma unroll
-                for (int i = 0; i < kPrefetchGroups; ++i) {
-                    const uint32_t j = lane + kWave * i;
-                    if (j >= full_lo && j < full_hi)
-                        sink.group(base + 8 * j, *reinterpret_cast<const uint2 *>(tile + 8 * j),
-                                   smv[i], fx[i]);
-                }
-            } else {
-#pragma unroll
-                for (int i = 0; i < kPrefetchGroups; ++i) {
-                    const uint32_t j = lane + kWave * i;
-                    if (j >= full_lo && j < full_hi)
-                        sink.group(base + 8 * j, *reinterpret_cast<const uint2 *>(tile + 8 * j),
-                                   smv[i], sink.fetch(base + 8 * j));
-                }
+            for (int i = 0; i < kPrefetchGroups; ++i) {
+                const uint32_t j = lane + kWave * i;
+                if (j >= full_lo && j < full_hi)
+                    sink.group(base + 8 * j, *reinterpret_cast<const uint2 *>(tile + 8 * j),
+                               smv[i], sink.fetch(base + 8 * j));
             }
             for (uint32_t j = lane + kWave * kPrefetchGroups; j < full_hi; j += kWave) {
                 const uint2 sm = load_sm8(a.signmant + base + 8 * j);
