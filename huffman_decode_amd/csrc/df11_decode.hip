@@ -161,21 +161,26 @@ __device__ __forceinline__ void group_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-__device__ __forceinline__ uint32_t join2(uint32_t e4, uint32_t s4, uint32_t sel_s, uint32_t sel_e) {
-    // two BF16 words from two exponent bytes and two sign|mantissa bytes:
-    // x = [s0 s0 s1 s1] supplies mantissa (bits 6:0, 22:16) and sign (15, 31);
-    // y = [.. e0 .. e1] >> 1 supplies the exponents at bits 14:7 and 30:23.
-    const uint32_t x = __builtin_amdgcn_perm(s4, s4, sel_s);
-    const uint32_t y = __builtin_amdgcn_perm(e4, e4, sel_e) >> 1;
-    return (x & 0x807F807Fu) | (y & ~0x807F807Fu);
+// Exponent bytes travel through LDS rotated right by one bit (bit 0 in bit
+// 7): the decode table holds them so, and a symbol taken from the 8-bit
+// tables is rotated with rotr8.  Then a BF16 word's high byte is
+// (e' & 0x7F) | (sm & 0x80) and its low byte (e' & 0x80) | (sm & 0x7F): one
+// v_bfi_b32 each per 4 words, and a v_perm_b32 interleaves them.
+__device__ __forceinline__ uint32_t rotr8(uint32_t e) {  // e: an 8-bit table entry or a byte
+    const uint32_t b = e & 0xFFu;
+    return ((b >> 1) | (b << 7)) & 0xFFu;
 }
 
 __device__ __forceinline__ uint4 join8(uint2 e, uint2 s) {
-    uint4 o;
-    o.x = join2(e.x, s.x, 0x01010000u, 0x010C000Cu);
-    o.y = join2(e.x, s.x, 0x03030202u, 0x030C020Cu);
-    o.z = join2(e.y, s.y, 0x01010000u, 0x010C000Cu);
-    o.w = join2(e.y, s.y, 0x03030202u, 0x030C020Cu);
+    const uint32_t hx = (e.x & 0x7F7F7F7Fu) | (s.x & 0x80808080u);
+    const uint32_t lx = (e.x & 0x80808080u) | (s.x & 0x7F7F7F7Fu);
+    const uint32_t hy = (e.y & 0x7F7F7F7Fu) | (s.y & 0x80808080u);
+    const uint32_t ly = (e.y & 0x80808080u) | (s.y & 0x7F7F7F7Fu);
+    uint4 o;  // words 2i, 2i+1: [low 2i, high 2i, low 2i+1, high 2i+1]
+    o.x = __builtin_amdgcn_perm(hx, lx, 0x05010400u);
+    o.y = __builtin_amdgcn_perm(hx, lx, 0x07030602u);
+    o.z = __builtin_amdgcn_perm(hy, ly, 0x05010400u);
+    o.w = __builtin_amdgcn_perm(hy, ly, 0x07030602u);
     return o;
 }
 
@@ -239,7 +244,7 @@ __device__ __forceinline__ uint32_t stage_codes(const uint8_t *lds_dec, const ui
         uint32_t inc = dv.x, syms = dv.y;
         if (dv.x < 0x10000u) {  // longer than the window: 8-bit tables, real bits
             const uint32_t e = lookup8(lut, __builtin_amdgcn_alignbit(dhi, dlo, acc), n_tables);
-            syms = e & 0xFFu;
+            syms = rotr8(e);
             inc = leaf_len(e) | 0x10000u;
         }
         const uint32_t at = acc >> 16;
@@ -334,7 +339,7 @@ __device__ __forceinline__ void decode_codes(const uint8_t *lds_dec, const uint1
             uint32_t inc = dv.x;
             if (dv.x < 0x10000u) {
                 const uint32_t e = lookup8(lut, __builtin_amdgcn_alignbit(dhi, dlo, acc), n_tables);
-                *(lds_u8 *)(uintptr_t)at_lds = (uint8_t)e;
+                *(lds_u8 *)(uintptr_t)at_lds = (uint8_t)rotr8(e);
                 inc = leaf_len(e) | 0x10000u;
             }
             acc += inc;
@@ -342,7 +347,7 @@ __device__ __forceinline__ void decode_codes(const uint8_t *lds_dec, const uint1
             uint32_t syms, k;
             if (dv.x < 0x10000u) {
                 const uint32_t e = lookup8(lut, __builtin_amdgcn_alignbit(dhi, dlo, acc), n_tables);
-                syms = e & 0xFFu;
+                syms = rotr8(e);
                 k = 1;
                 acc += leaf_len(e) | 0x10000u;
             } else {
@@ -381,7 +386,7 @@ __device__ __forceinline__ void rewrite_head(const uint8_t *lds_dec, const uint1
         uint32_t k, b, syms;
         if (dv.x < 0x10000u) {
             const uint32_t e = lookup8(lut, wd, n_tables);
-            syms = e & 0xFFu;
+            syms = rotr8(e);
             k = 1;
             b = leaf_len(e);
         } else {
@@ -397,8 +402,9 @@ __device__ __forceinline__ void rewrite_head(const uint8_t *lds_dec, const uint1
 }
 
 // One BF16 word from an exponent byte and a sign|mantissa byte.
+// one BF16 word from a rotated exponent byte and its sign|mantissa byte
 __device__ __forceinline__ uint32_t join1(uint32_t e, uint32_t sm) {
-    return ((sm & 0x80u) << 8) | ((e & 0xFFu) << 7) | (sm & 0x7Fu);
+    return ((((e & 0x7Fu) | (sm & 0x80u)) << 8) | (e & 0x80u) | (sm & 0x7Fu)) & 0xFFFFu;
 }
 
 // What a decoded block's BF16 words go to.  The kernel body calls

@@ -217,7 +217,8 @@ uint32_t table_leaf(const uint16_t *lut, uint32_t w, uint32_t n_tables) {
 // The multi-code decode table for the kernel.  Entry i covers the codes at
 // the start of window i that end within its first width = min(max_len - 1,
 // kDecodeTableBits) bits, at most four.  It stores their total length |
-// their number << 16, then their symbols one per byte (unused bytes 0).
+// their number << 16, then their symbols one per byte, each rotated right
+// by one bit (unused bytes 0).
 // All ones is a prefix of the longest code, so a window of ones never
 // completes one here.  A code longer than the window leaves the entry empty,
 // and the kernel resolves it through the 8-bit tables.  The next code of
@@ -232,7 +233,10 @@ void build_decode_table(const uint16_t *lut, uint32_t n_tables, uint32_t max_len
             const uint32_t e = first[i >> pos];
             const uint32_t len = ((e >> 8) & 31u) + 1;
             if (pos + len > width) break;
-            syms |= (e & 0xFFu) << (8 * k);
+            // the symbol (an exponent byte) rotated right by one bit, the form
+            // the kernel joins with the sign|mantissa byte
+            const uint32_t sym = e & 0xFFu;
+            syms |= (((sym >> 1) | (sym << 7)) & 0xFFu) << (8 * k);
             pos += len;
             ++cnt;
         }

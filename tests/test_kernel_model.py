@@ -225,7 +225,8 @@ def test_model_longest_codes():
 def test_host_decode_table_matches_model(kind):
     """The table image ends with the multi-code decode table that the kernel
     copies to LDS (built by the host library).  Every entry must be the
-    model's: total length | code count << 16, then the symbols, unused bytes 0.
+    model's: total length | code count << 16, then the symbols, each rotated
+    right by one bit (the form the kernel joins), unused bytes 0.
     The cases cover short codes, a flat code, the one-symbol code (no code
     fits the window, every entry is empty) and codes up to 32 bits."""
     if kind == "fibonacci_33":
@@ -237,7 +238,8 @@ def test_host_decode_table_matches_model(kind):
     lut = enc.luts.view(np.uint16)
     tail = enc.luts[n_tables * 512:].view(np.uint32)
     assert tail.size == 2 * (1 << DECODE_BITS)
+    rotr8 = lambda e: ((e >> 1) | (e << 7)) & 0xFF  # the kernel's form of an exponent byte
     for i, (pos, k, syms) in enumerate(_table(lut, n_tables, enc.codebook.max_len)):
-        packed = sum(int(s) << (8 * j) for j, s in enumerate(syms[:k]))
+        packed = sum(rotr8(int(s)) << (8 * j) for j, s in enumerate(syms[:k]))
         assert int(tail[2 * i]) == pos | (k << 16), (kind, i)
         assert int(tail[2 * i + 1]) == packed, (kind, i)
