@@ -35,6 +35,9 @@
 //    with more codes than a slot holds (only near-flat streams of 1- and
 //    2-bit codes) send their wave down the page's own route: decode the real
 //    bits again, straight into the tile;
+//  * exponent bytes are kept rotated right by one bit from the decode table
+//    to the merge, so that joining them with sign|mantissa bytes takes only
+//    bit-field inserts and byte permutes (no shifts);
 //  * the merge joins 8 exponents with 8 prefetched sign|mantissa bytes per
 //    lane and writes one 16-byte store (the fused variant instead takes the
 //    dot products of the 8 words with each input vector, with a copy of the
