@@ -845,22 +845,36 @@ __device__ __forceinline__ void decode_blocks(const DecodeArgs &a, Sink &sink) {
             const int32_t d = (int32_t)(blk - b);  // block indices are below 2^27
             return d > 1 ? (1 << 30) : (d < -1 ? -(1 << 30) : d * 4096 + (int32_t)rem);
         };
-        const int32_t lane_bit = (int32_t)(lane * DF11_SLICE_BITS);
-        const int32_t rel = from_block(a.stop_blk, a.stop_rem) - lane_bit;
-        // codes of this lane start in [gap, lim); the last one ends at `end`:
-        // the next slice's first code start, or the stream's end for the lane
-        // holding the final code
-        const uint32_t lim = rel <= 0 ? 0u : (rel >= 64 ? 64u : (uint32_t)rel);
-        const uint32_t end = rel > 0 && rel <= 64
-                                 ? (uint32_t)(from_block(a.end_blk, a.end_rem) - lane_bit)
-                                 : 64u + gap_next;
+        // codes of a lane start in [gap, lim); the last one ends at `end`: the
+        // next slice's first code start, or the stream's end for the lane
+        // holding the final code.  f* are the slice's dwords with the bits from
+        // `end` on set to 1.  A block whose every slice lies before the stop
+        // bit (all but the stream's last block or two) has lim = 64 and end =
+        // 64 + gap_next in every lane, which leaves only the third dword to pad
+        // (wave-uniform branch)
+        const int32_t stop_at = from_block(a.stop_blk, a.stop_rem);
+        uint32_t lim, f0, f1, f2;
+        if (stop_at > kWave * DF11_SLICE_BITS) {
+            lim = 64u;
+            f0 = d0;
+            f1 = d1;
+            f2 = d2 | (0xFFFFFFFFu << gap_next);
+        } else {
+            const int32_t lane_bit = (int32_t)(lane * DF11_SLICE_BITS);
+            const int32_t rel = stop_at - lane_bit;
+            lim = rel <= 0 ? 0u : (rel >= 64 ? 64u : (uint32_t)rel);
+            const uint32_t end = rel > 0 && rel <= 64
+                                     ? (uint32_t)(from_block(a.end_blk, a.end_rem) - lane_bit)
+                                     : 64u + gap_next;
+            f0 = pad_ones(d0, (int)end, 0);
+            f1 = pad_ones(d1, (int)end, 32);
+            f2 = pad_ones(d2, (int)end, 64);
+        }
 
         // ---- phase 1: decode into the lane's staging slot, counting
         const uint32_t slot = tile_addr + kStageBase + lane * kStageStride;
         const uint32_t cnt =
-            lim ? stage_codes(lds_dec, lut, a.n_tables, d0, d1, d2, pad_ones(d0, (int)end, 0),
-                              pad_ones(d1, (int)end, 32), pad_ones(d2, (int)end, 64), gap, lim,
-                              slot)
+            lim ? stage_codes(lds_dec, lut, a.n_tables, d0, d1, d2, f0, f1, f2, gap, lim, slot)
                 : 0u;
 
         // wave-wide prefix sum of the counts

@@ -243,3 +243,29 @@ def test_host_decode_table_matches_model(kind):
         packed = sum(rotr8(int(s)) << (8 * j) for j, s in enumerate(syms[:k]))
         assert int(tail[2 * i]) == pos | (k << 16), (kind, i)
         assert int(tail[2 * i + 1]) == packed, (kind, i)
+
+
+def _pad_ones(d, end, base):
+    keep = end - base
+    if keep >= 32:
+        return d
+    if keep <= 0:
+        return 0xFFFFFFFF
+    return (d | (0xFFFFFFFF << keep)) & 0xFFFFFFFF
+
+
+@pytest.mark.parametrize("stop_at", [4097, 4096 + 4095, 1 << 30])
+def test_block_before_stop_needs_only_third_dword_padded(stop_at):
+    """The kernel's shortcut for a block wholly before the stop bit (every lane
+    lim = 64, end = 64 + next gap) equals the per-lane limits and padding."""
+    rng = np.random.default_rng(stop_at & 0xFFFF)
+    for lane in range(64):
+        rel = stop_at - 64 * lane
+        for gap_next in range(32):
+            d = [int(v) for v in rng.integers(0, 1 << 32, 3, dtype=np.uint64)]
+            assert rel > 64  # so the per-lane rule takes end = 64 + gap_next
+            lim, end = min(64, rel), 64 + gap_next
+            general = (lim, _pad_ones(d[0], end, 0), _pad_ones(d[1], end, 32),
+                       _pad_ones(d[2], end, 64))
+            shortcut = (64, d[0], d[1], (d[2] | (0xFFFFFFFF << gap_next)) & 0xFFFFFFFF)
+            assert general == shortcut
