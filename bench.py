@@ -6,19 +6,20 @@ weights (one code book, one stream), from DF11 arrays resident in HBM to BF16
 words in HBM.  The default workload is the Llama-3.1-8B-shaped block (q/o
 4096x4096, k/v 1024x4096, gate/up 14336x4096, down 4096x14336; 218,103,808
 weights, N(0, sigma_m) with per-matrix sigma jitter).  R identical encoded
-copies at different addresses are decoded in turn so that the 256 MB
-Infinity Cache cannot hold a step's inputs from the previous use.
+copies at different addresses, each with its own output buffer, are decoded
+in turn (R large enough that they span three times the 256 MB Infinity
+Cache) so that a launch finds none of its bytes cached by the launch before.
 
 Prints one JSON line.  value = effective GB/s = (algorithmic bytes read +
 2n bytes written) / device time of one launch, where the bytes read are the
 code stream (total_bits / 8), the 5-bit gaps, the block positions, the n
-sign|mantissa bytes and the lookup tables.
+sign|mantissa bytes and the lookup tables.  roofline.ceiling_gbs is the rate
+of a traffic-only kernel (df11_stream_ceiling) moving the same bytes on the
+same buffers, timed right after the decode.
 """
 from __future__ import annotations
 
 import argparse
-import hashlib
-import re
 import json
 import os
 import sys
@@ -28,19 +29,18 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E peak (vendor figure)
-KERNEL_SOURCE = os.path.join(ROOT, "huffman_decode_amd", "csrc", "df11_decode.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "df11_decode_llama8b_block_traffic.txt")
 
 
-def kernel_hash() -> str:
-    """Hash of the kernel source's code: comments and whitespace are dropped
-    first, so that only a change to the code itself retires the counters."""
-    with open(KERNEL_SOURCE) as f:
-        text = f.read()
-    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
-    text = re.sub(r"//[^\n]*", " ", text)
-    text = "".join(text.split())
-    return hashlib.sha256(text.encode()).hexdigest()[:16]
+def kernel_hash(name: str = "df11_decode_kernel") -> str | None:
+    """Hash of a kernel's machine code in the built library (written by the
+    build next to it): counters stay valid exactly as long as it is equal."""
+    path = os.path.join(ROOT, "huffman_decode_amd", "libdf11.kernels.json")
+    try:
+        with open(path) as f:
+            return json.load(f).get(name)
+    except (OSError, ValueError):
+        return None
 
 
 def algorithmic_bytes(enc) -> tuple[int, int]:
@@ -67,7 +67,7 @@ def measured_traffic(n_launch_bytes: int):
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
                 vals[k.strip()] = v.strip()
-    if vals.get("kernel_sha256_16") != kernel_hash():
+    if vals.get("kernel_isa_sha16") != kernel_hash():
         return None
     try:
         if int(vals["algorithmic_bytes_per_launch"]) != int(n_launch_bytes):
@@ -77,22 +77,75 @@ def measured_traffic(n_launch_bytes: int):
         return None
 
 
-def cpu_baseline(wlx, enc) -> dict:
-    """The oracle's serial bit-by-bit decode + join over the whole block, one core."""
+def host_threads() -> int:
+    """Host threads for the parallel oracle leg: the CPUs this process may run
+    on, at most 16 (a GPU's share of its host)."""
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        avail = os.cpu_count() or 1
+    return max(1, min(avail, 16))
+
+
+def _gap_fields(gaps_packed, slices):
+    """5-bit gap fields at the given slice indices (packed least significant
+    bit first)."""
     import numpy as np
+    bits = 5 * np.asarray(slices, dtype=np.int64)
+    lo = gaps_packed[bits >> 3].astype(np.uint32)
+    hi = gaps_packed[(bits >> 3) + 1].astype(np.uint32)
+    return (((hi << 8) | lo) >> (bits & 7).astype(np.uint32)) & 31
+
+
+def cpu_baseline(wlx, enc) -> dict:
+    """The oracle's bit-by-bit decode + join of the whole block: serially on one
+    core, and split at block starts over the host's cores (each chunk of blocks
+    decodes from its first slice's gap offset on its own, which is the chunk
+    decode property the DF11 format rests on).  Both are checked bit-exact."""
+    import numpy as np
+    from concurrent.futures import ThreadPoolExecutor
     import oracle
     n = int(enc.sizes.n)
-    t0 = time.perf_counter()
-    ex, end = oracle.decode(enc.stream, int(enc.sizes.total_bits), 0, n, enc.codebook.lengths)
-    w = oracle.join_bf16(ex, enc.signmant[:n])
-    dt = time.perf_counter() - t0
-    ok = bool(np.array_equal(w, wlx.weights)) and end == int(enc.sizes.total_bits)
+    total = int(enc.sizes.total_bits)
+    lengths = enc.codebook.lengths
     rd, wr = algorithmic_bytes(enc)
-    return {"value": round((rd + wr) / dt / 1e9, 4), "unit": "GB/s", "cores": 1,
-            "kind": "oracle", "gweights_per_s": round(n / dt / 1e9, 5), "seconds": round(dt, 2),
-            "bit_exact": ok,
-            "sample": f"whole {wlx.name} ({n} weights): oracle serial tree-walk decode "
-                      f"of every code from bit 0, then BF16 join, 1 thread"}
+
+    t0 = time.perf_counter()
+    ex, end = oracle.decode(enc.stream, total, 0, n, lengths)
+    w = oracle.join_bf16(ex, enc.signmant[:n])
+    dt1 = time.perf_counter() - t0
+    ok1 = bool(np.array_equal(w, wlx.weights)) and end == total
+    del ex, w
+
+    threads = host_threads()
+    nb = int(enc.sizes.n_blocks)
+    edges = np.linspace(0, nb, min(nb, 8 * threads) + 1).astype(np.int64)
+    starts = 4096 * edges[:-1] + _gap_fields(enc.gaps, 64 * edges[:-1]).astype(np.int64)
+    out = np.empty(n, np.uint16)
+    bp = enc.block_pos.astype(np.int64)
+
+    def chunk(i):
+        b0, b1 = int(edges[i]), int(edges[i + 1])
+        p0, p1 = int(bp[b0]), int(bp[b1])
+        stop = 4096 * b1 if b1 < nb else total
+        e = oracle.decode_range(enc.stream, total, int(starts[i]), stop, lengths, p1 - p0)
+        out[p0:p1] = oracle.join_bf16(e, enc.signmant[p0:p1])
+        return e.size == p1 - p0
+
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(max_workers=threads) as pool:
+        sizes_ok = all(pool.map(chunk, range(len(edges) - 1)))
+    dtn = time.perf_counter() - t0
+    okn = sizes_ok and bool(np.array_equal(out, wlx.weights))
+    return {"value": round((rd + wr) / dtn / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle", "gweights_per_s": round(n / dtn / 1e9, 5),
+            "seconds": round(dtn, 3), "bit_exact": okn and ok1,
+            "host_cpu_count": os.cpu_count(),
+            "one_core": {"value": round((rd + wr) / dt1 / 1e9, 4), "unit": "GB/s", "cores": 1,
+                         "gweights_per_s": round(n / dt1 / 1e9, 5), "seconds": round(dt1, 3)},
+            "sample": f"whole {wlx.name} ({n} weights): oracle tree-walk decode of every "
+                      f"code, then BF16 join; value: {len(edges) - 1} chunks of whole blocks "
+                      f"on {threads} threads; one_core: serial from bit 0"}
 
 
 def run_copy(args) -> int:
@@ -148,7 +201,10 @@ def gemm_ratios(wlx, out, decode_ms, stream, batches=(1, 2, 4, 64), reps=10) -> 
         s1.record(stream)
         torch.cuda.synchronize()
         gms = s0.elapsed_time(s1) / reps
-        res[f"batch{b}"] = {"gemm_ms": round(gms, 5), "decode_over_gemm": round(decode_ms / gms, 4)}
+        # bytes a BF16 GEMM moves: the weights, x and y (bf16)
+        moved = sum(2 * w.numel() + 2 * b * (w.shape[0] + w.shape[1]) for w in mats)
+        res[f"batch{b}"] = {"gemm_ms": round(gms, 5), "decode_over_gemm": round(decode_ms / gms, 4),
+                            "gemm_gbs": round(moved / (gms * 1e-3) / 1e9, 1)}
     return res
 
 
@@ -389,20 +445,23 @@ def main() -> int:
                     help="untimed steps first (default 300 for decode and copy: the GPU's "
                          "clocks take ~100 back-to-back launches to ramp up; else 3)")
     ap.add_argument("--workload", default="llama8b_block")
-    ap.add_argument("--copies", type=int, default=3,
-                    help="rotating encoded copies (defeats the Infinity Cache)")
+    ap.add_argument("--copies", type=int, default=0,
+                    help="rotating encoded copies and output buffers (0: enough that they "
+                         "span at least 768 MB, three times the 256 MB Infinity Cache, and "
+                         "at least 3)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-gemm", action="store_true", help="skip the decode/GEMM ratios")
-    ap.add_argument("--mode", choices=("decode", "copy", "stack", "encode", "offload"),
+    ap.add_argument("--mode", choices=("decode", "copy", "stack", "encode", "offload", "ceiling"),
                     default="decode",
-                    help="copy: time a plain device copy of --copy-mib MiB instead; "
+                    help="ceiling: only the traffic-only kernel on the workload's bytes; "
+                         "copy: time a plain device copy of --copy-mib MiB instead; "
                          "stack: decode/GEMM schedules over the 32-block 8B-shaped stack; "
                          "encode: host encoder throughput (no GPU); "
                          "offload: blocks from pinned host memory, copied and decoded in turn")
     ap.add_argument("--layers", type=int, default=32, help="blocks in the stack mode")
     ap.add_argument("--copy-mib", type=int, default=1024)
     args = ap.parse_args()
-    fast = args.mode in ("decode", "copy")
+    fast = args.mode in ("decode", "copy", "ceiling")
     if args.steps is None:
         args.steps = 100 if fast else 20
     if args.warmup is None:
@@ -439,32 +498,69 @@ def main() -> int:
     enc = hd.encode(wlx.weights)
     t_enc = time.perf_counter() - t0
     n = enc.n
-    copies = [hd.to_device(enc, dev) for _ in range(max(1, args.copies))]
-    out = torch.empty(n, dtype=torch.bfloat16, device=dev)
+    rd, wr = algorithmic_bytes(enc)
+    # rotating copies of the inputs and of the output, so that a launch finds
+    # nothing of its bytes in the 256 MB Infinity Cache from the launch before
+    n_copies = args.copies or max(3, -(-768_000_000 // (rd + wr)))
+    copies = [hd.to_device(enc, dev) for _ in range(n_copies)]
+    outs = [torch.empty(n, dtype=torch.bfloat16, device=dev) for _ in range(n_copies)]
     stream = torch.cuda.current_stream(dev)
 
-    for k in range(args.warmup):
-        hd.df11_decode(copies[k % len(copies)], out, stream)
-    torch.cuda.synchronize()
+    def timed(launch, steps, warmup):
+        """Average duration of `launch(k)` over `steps` back-to-back launches
+        between one pair of events on the launch stream (no markers between
+        launches, which would add their own gaps)."""
+        for k in range(warmup):
+            launch(k)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        w0 = time.perf_counter()
+        e0.record(stream)
+        for k in range(steps):
+            launch(k)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps, time.perf_counter() - w0
 
-    # Timed region: K launches back to back between one pair of events on the
-    # launch stream (no markers between launches, which would add their own
-    # gaps); the average launch duration is the region's time over K.
-    t_begin, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    t_begin.record(stream)
-    for k in range(args.steps):
-        hd.df11_decode(copies[k % len(copies)], out, stream)
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    avg_ms = t_begin.elapsed_time(t_end) / args.steps
-    rd, wr = algorithmic_bytes(enc)
+    # the traffic-only kernel on the same bytes: sign|mantissa and the output
+    # with the decode's widths, the rest of the decode's reads from a buffer
+    # of exactly that size (per copy)
+    n8 = n & ~7
+    b_bytes = (rd - n) // 16 * 16
+    extras = [torch.empty(b_bytes, dtype=torch.uint8, device=dev).fill_(k + 1)
+              for k in range(n_copies)]
+
+    def ceiling(k):
+        c = k % n_copies
+        hd.df11_stream_ceiling(copies[c].tensors["signmant"], extras[c], outs[c], n8, 0, stream)
+
+    if args.mode == "ceiling":
+        c_ms, _ = timed(ceiling, args.steps, args.warmup)
+        cb = n8 + b_bytes + 2 * n8
+        print(json.dumps({"mode": "ceiling", "workload": args.workload, "kernel_ms": round(c_ms, 5),
+                          "bytes": cb, "GBps": round(cb / (c_ms * 1e-3) / 1e9, 1),
+                          "copies": n_copies}), flush=True)
+        return 0
+
+    def decode(k):
+        c = k % n_copies
+        hd.df11_decode(copies[c], outs[c], stream)
+
+    avg_ms, wall = timed(decode, args.steps, args.warmup)
     gbs = (rd + wr) / (avg_ms * 1e-3) / 1e9
     orig = torch.from_numpy(wlx.weights.view(np.int16)).to(dev)
-    bit_exact = bool(torch.equal(out.view(torch.int16), orig))
+    # every output buffer the launches wrote (the k-th launch writes buffer k % copies)
+    written = outs[: min(n_copies, max(args.steps, args.warmup))]
+    bit_exact = all(bool(torch.equal(o.view(torch.int16), orig)) for o in written)
+    del orig
     traffic = measured_traffic(rd + wr)
+    # the ceiling, timed right after the decode on the same copies and buffers
+    c_ms, _ = timed(ceiling, args.steps, 20)
+    ceiling_gbs = (n8 + b_bytes + 2 * n8) / (c_ms * 1e-3) / 1e9
+    for c in range(n_copies):  # the decoded weights again, for the GEMM ratios
+        decode(c)
+    torch.cuda.synchronize()
+    out = outs[0]
 
     line = {
         "metric": "df11_decode effective HBM GB/s + Gweights/s on 1 MI355X; % of HBM roofline",
@@ -489,11 +585,16 @@ def main() -> int:
                    "total_code_bits": int(enc.sizes.total_bits),
                    "max_code_len": int(enc.codebook.max_len),
                    "n_tables": int(enc.codebook.n_tables),
-                   "rotating_copies": len(copies), "host_encode_s": round(t_enc, 2)},
+                   "rotating_copies": n_copies,
+                   "resident_bytes_rotated": n_copies * (rd + wr),
+                   "host_encode_s": round(t_enc, 2)},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
-                     "bytes_per_launch": {"read": rd, "written": wr}},
+                     "bytes_per_launch": {"read": rd, "written": wr},
+                     "ceiling_gbs": round(ceiling_gbs, 1),
+                     "ceiling_ms": round(c_ms, 5),
+                     "frac_of_ceiling": round(gbs / ceiling_gbs, 4)},
     }
     if not args.no_gemm:
         line["decode_vs_gemm"] = gemm_ratios(wlx, out, avg_ms, stream)
@@ -501,11 +602,16 @@ def main() -> int:
         # 2 and 4) against the BF16 GEMMs on resident weights and against
         # decoding first and then running those GEMMs
         fused = {}
+        nx = sum(m.cols for m in wlx.matrices)
+        ny = sum(m.rows for m in wlx.matrices)
         for b in (1, 2, 4):
             f = fused_gemv(wlx, copies, stream) if b == 1 else fused_gemm(wlx, copies, stream, b)
             g = line["decode_vs_gemm"][f"batch{b}"]["gemm_ms"]
             f["over_bf16_gemm"] = round(f["fused_ms"] / g, 4)
             f["over_decode_then_gemm"] = round(f["fused_ms"] / (avg_ms + g), 4)
+            # the bytes a fused product must move: the compressed weights, x
+            # (bf16) and y (fp32)
+            f["fused_gbs"] = round((rd + 2 * b * nx + 4 * b * ny) / (f["fused_ms"] * 1e-3) / 1e9, 1)
             fused[f"batch{b}"] = f
         line["decode_vs_gemm"]["fused"] = fused
     if not args.no_cpu_baseline:

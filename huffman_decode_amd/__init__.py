@@ -106,6 +106,8 @@ def _load():
             lib.df11_decode_gemm.argtypes = [ctypes.POINTER(DeviceStream), ctypes.POINTER(GemvMatrix),
                                              _U32, _P, _U32, _U64, _P, _U64, _P, _U64, _P]
             lib.df11_decode_gemm.restype = ctypes.c_int
+        lib.df11_stream_ceiling.argtypes = [_P, _P, _U64, _P, _U64, _U32, _P]
+        lib.df11_stream_ceiling.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -315,16 +317,36 @@ def df11_gemv_workspace_bytes(dev: DeviceEncoded) -> int:
     return int(_load().df11_gemv_workspace_bytes(ctypes.byref(dev.desc)))
 
 
+def _matrix_ends(mats: list[GemvMatrix]) -> tuple[int, int]:
+    """(elements of x, elements of y) that one vector's matrices reach."""
+    x_end = max((int(m.x_offset) + int(m.cols) for m in mats), default=0)
+    y_end = max((int(m.y_offset) + int(m.rows) for m in mats), default=0)
+    return x_end, y_end
+
+
+def _same_device(dev: DeviceEncoded, **tensors) -> None:
+    where = dev.tensors["stream"].device
+    for name, t in tensors.items():
+        if t.device != where:
+            raise ValueError(f"{name} is on device {t.device}, the encoded tensor on {where}")
+
+
 def df11_decode_gemv(dev: DeviceEncoded, mats: list[GemvMatrix], x, y, workspace,
                      stream=None) -> None:
     """Enqueue y = W x for every matrix of ``dev`` (x a bfloat16 and y a float32
     CUDA tensor, workspace a CUDA tensor of at least df11_gemv_workspace_bytes
-    bytes)."""
+    bytes).  x and y must reach every matrix's inputs and results (the C call
+    receives no sizes for them, so they are checked here)."""
     import torch
     if x.dtype != torch.bfloat16 or not x.is_contiguous():
         raise ValueError("x must be a contiguous bfloat16 tensor")
     if y.dtype != torch.float32 or not y.is_contiguous():
         raise ValueError("y must be a contiguous float32 tensor")
+    _same_device(dev, x=x, y=y, workspace=workspace)
+    x_end, y_end = _matrix_ends(mats)
+    if x.numel() < x_end or y.numel() < y_end:
+        raise ValueError(f"x holds {x.numel()} and y {y.numel()} elements; the matrices "
+                         f"need {x_end} and {y_end}")
     if stream is None:
         stream = torch.cuda.current_stream(y.device)
     arr = (GemvMatrix * len(mats))(*mats)
@@ -351,6 +373,11 @@ def df11_decode_gemm(dev: DeviceEncoded, mats: list[GemvMatrix], x, y, workspace
         raise ValueError("y must be a [batch, ny] float32 tensor with unit column stride")
     if x.shape[0] != y.shape[0]:
         raise ValueError("x and y must hold the same number of vectors")
+    _same_device(dev, x=x, y=y, workspace=workspace)
+    x_end, y_end = _matrix_ends(mats)
+    if x.shape[1] < x_end or y.shape[1] < y_end:
+        raise ValueError(f"x rows hold {x.shape[1]} and y rows {y.shape[1]} elements; the "
+                         f"matrices need {x_end} and {y_end}")
     if stream is None:
         stream = torch.cuda.current_stream(y.device)
     arr = (GemvMatrix * len(mats))(*mats)
@@ -358,3 +385,20 @@ def df11_decode_gemm(dev: DeviceEncoded, mats: list[GemvMatrix], x, y, workspace
     _check("df11_decode_gemm", _load().df11_decode_gemm(
         ctypes.byref(dev.desc), arr, len(mats), x.data_ptr(), x.shape[0], x.stride(0),
         y.data_ptr(), y.stride(0), workspace.data_ptr(), nbytes, stream.cuda_stream))
+
+
+# ------------------------------------------------------------ measurement aid
+
+def df11_stream_ceiling(a, b, out, n: int, max_groups: int = 0, stream=None) -> None:
+    """Enqueue the traffic-only kernel: reads a[0..n) bytes and all of b,
+    writes n 16-bit words to out (see include/df11.h).  a, b, out are CUDA
+    tensors (b may be None)."""
+    import torch
+    b_bytes = 0 if b is None else b.numel() * b.element_size()
+    if a.numel() * a.element_size() < n or out.numel() * out.element_size() < 2 * n:
+        raise ValueError("a or out is smaller than n")
+    if stream is None:
+        stream = torch.cuda.current_stream(out.device)
+    _check("df11_stream_ceiling", _load().df11_stream_ceiling(
+        a.data_ptr(), 0 if b is None else b.data_ptr(), b_bytes, out.data_ptr(), n, max_groups,
+        stream.cuda_stream))

@@ -56,12 +56,8 @@
 
 namespace {
 
-#ifndef DF11_WAVES_PER_GROUP
-#define DF11_WAVES_PER_GROUP 8
-#endif
-
 constexpr int kWave = 64;
-constexpr int kWavesPerGroup = DF11_WAVES_PER_GROUP;
+constexpr int kWavesPerGroup = 8;
 constexpr int kGroupThreads = kWave * kWavesPerGroup;
 constexpr int kMaxBlockCodes = DF11_BLOCK_SLICES * DF11_SLICE_BITS;  // all 1-bit codes
 // staging: lane t's phase-1 exponents at byte 4 + 40 t of its wave's LDS
@@ -91,15 +87,11 @@ constexpr int kXcds = 8;
 // table image, copied to LDS by each workgroup): index width
 constexpr int kDecodeBits = (int)df11_internal::kDecodeTableBits;
 constexpr int kDecodeBytes = (int)df11_internal::kDecodeTableBytes;
-constexpr int kMaxSymbolsPerStep = 4;
 constexpr int kTilesBytes = kWavesPerGroup * kTileBytes;
 constexpr int kStaticLds = kTilesBytes + kDecodeBytes;
 static_assert(kTilesBytes < 0x10000, "tile addresses must fit 16 bits");
-#ifndef DF11_PREFETCH_GROUPS
-#define DF11_PREFETCH_GROUPS 2
-#endif
 // sign|mantissa groups of 8 per lane loaded up front
-constexpr int kPrefetchGroups = DF11_PREFETCH_GROUPS;
+constexpr int kPrefetchGroups = 2;
 static_assert(kPrefetchGroups >= 1, "at least one group is prefetched");
 
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
@@ -670,10 +662,8 @@ struct DotSink {
 
 // at least 6 waves per SIMD: keeps the register budget at 80 VGPRs, the
 // most that still lets 3 workgroups of 8 waves share a CU
-#ifndef DF11_WAVES_PER_EU
-#define DF11_WAVES_PER_EU 6
-#endif
-#define DF11_OCCUPANCY_HINT __attribute__((amdgpu_waves_per_eu(DF11_WAVES_PER_EU)))
+constexpr int kWavesPerEu = 6;
+#define DF11_OCCUPANCY_HINT __attribute__((amdgpu_waves_per_eu(kWavesPerEu)))
 template <class Sink>
 __device__ __forceinline__ void decode_blocks(const DecodeArgs &a, Sink &sink) {
     // LDS: per-wave regions (staging slots, then the exponent tile) | decode
@@ -1021,12 +1011,12 @@ __global__ __launch_bounds__(kGroupThreads) DF11_OCCUPANCY_HINT void df11_decode
 // it keeps the decode's budget of 80 VGPRs (3 workgroups per CU); 4 and 8
 // vectors need more registers and run 2 workgroups per CU.
 template <int kB> struct GemmOccupancy {
-    static constexpr int kWavesPerEu = kB <= 2 ? DF11_WAVES_PER_EU : 4;
+    static constexpr int kValue = kB <= 2 ? kWavesPerEu : 4;
 };
 
 template <int kB>
 __global__ __launch_bounds__(kGroupThreads)
-__attribute__((amdgpu_waves_per_eu(GemmOccupancy<kB>::kWavesPerEu)))
+__attribute__((amdgpu_waves_per_eu(GemmOccupancy<kB>::kValue)))
 void df11_gemm_kernel(DecodeArgs a, GemvArgs g) {
     // the matrix table goes to LDS with constant indices (indexing the kernel
     // argument at run time would make the compiler copy it to scratch); the
@@ -1188,9 +1178,6 @@ int launch_groups(K kernel, int which, int dev, uint32_t n_tables, uint32_t n_bl
                                                          lds_bytes(n_tables)) != hipSuccess)
             return DF11_ERR_HIP;
         if (occ <= 0) return DF11_ERR_TABLES;
-#ifdef DF11_MAX_OCCUPANCY
-        occ = occ < DF11_MAX_OCCUPANCY ? occ : DF11_MAX_OCCUPANCY;
-#endif
         g_occ[which][dev][n_tables].store(occ, std::memory_order_relaxed);
     }
     // a multiple of the XCD count, no more than there are blocks to share

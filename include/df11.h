@@ -118,14 +118,24 @@ typedef struct df11_sizes {
     uint32_t reserved;
 } df11_sizes;
 
-/* Errors: ARG, FORMAT (hist does not sum to n or holds a symbol without a
+/* Sizes of the encoded arrays (section "Architecture": the code stream cut
+ * into 8-byte per-thread slices, one Gaps field per slice and one
+ * BlockOutputPos entry per block; section "How it works": the stream holds
+ * sum over symbols of count x code length bits), from the histogram alone.
+ * Errors: ARG, FORMAT (hist does not sum to n or holds a symbol without a
  * code). */
 int df11_encoded_sizes(const uint64_t hist[256], uint64_t n, const df11_codebook *cb,
                        df11_sizes *out);
 
-/* Encode n BF16 words (host memory).  Writes stream, packed gaps, block_pos,
- * signmant (padding bytes zeroed) and fills *out.  n_threads = 0 picks the
- * number of hardware threads; the output does not depend on it.
+/* Encode n BF16 words (host memory).  Section "How it works": each weight is
+ * split into its exponent byte and its sign|mantissa byte; the exponent's
+ * canonical code is appended to the stream most significant code bit first;
+ * the sign|mantissa byte is stored raw.  Section "Architecture": while the
+ * codes are emitted, each slice's Gaps field (offset of the first code that
+ * starts in it) and each block's BlockOutputPos (index of its first code) are
+ * recorded.  Writes stream, packed gaps, block_pos, signmant (padding bytes
+ * zeroed) and fills *out.  n_threads = 0 picks the number of hardware
+ * threads; the output does not depend on it.
  * Errors: ARG, BUFSIZE, FORMAT (a weight's exponent has no code). */
 int df11_encode(const uint16_t *bf16, uint64_t n, const df11_codebook *cb,
                 uint8_t *stream, uint64_t stream_cap,
@@ -158,12 +168,18 @@ typedef struct df11_device_stream {
 } df11_device_stream;
 
 /* Decode on the GPU: out[0..n) = the original BF16 words, bit for bit.
- * Two-phase wave-per-block decode (section "Architecture", two-phase kernel):
- * per 64-bit slice, count codes; wave prefix sum of the counts; decode again
- * into an LDS tile; merge each exponent with its sign|mantissa byte; write
- * coalesced 16-byte stores.  Enqueued on hip_stream (a hipStream_t; NULL =
- * the null stream) and returns without waiting.  out must be 16-byte
- * aligned; stream, signmant 8-byte; gaps, block_pos 4-byte.
+ * The two-phase kernel of section "Architecture", one wavefront per 512-byte
+ * block: each lane starts at its slice's Gaps offset and decodes the codes
+ * that start in its slice once, into a private LDS staging slot (the number
+ * decoded is its count); a wave prefix sum of the counts, offset by the
+ * block's BlockOutputPos, gives every lane its output position; the staged
+ * exponents move to an LDS tile at those positions (blocks whose lanes hold
+ * more than 32 or, short of the block's end, fewer than 3 codes instead
+ * decode their slices a second time straight into the tile, the page's own
+ * route); each exponent is joined with its sign|mantissa byte and the
+ * words are written with coalesced 16-byte stores.  Enqueued on hip_stream
+ * (a hipStream_t; NULL = the null stream) and returns without waiting.  out
+ * must be 16-byte aligned; stream, signmant 8-byte; gaps, block_pos 4-byte.
  * Errors: ARG, BUFSIZE, FORMAT, TABLES, HIP.  A corrupt stream is not
  * detected in general (a flipped bit silently desynchronises the decoder);
  * it never makes the kernel read or write outside the stated buffers. */
@@ -231,6 +247,22 @@ int df11_decode_gemm(const df11_device_stream *s, const df11_gemv_matrix *mats, 
                      const uint16_t *x, uint32_t batch, uint64_t x_stride, float *y,
                      uint64_t y_stride, void *workspace, uint64_t workspace_bytes,
                      void *hip_stream);
+
+/* ------------------------------------------------------- measurement aid */
+
+/* Streaming ceiling: a kernel that moves the bytes of one df11_decode launch
+ * and does no decoding, as the floor its time is measured against (not part
+ * of the decode path).  Reads a[0..n) with one 8-byte load per 8 words (as
+ * the decode reads sign|mantissa bytes) and b[0..b_bytes) with 16-byte loads
+ * spread evenly over those groups; writes out[0..n) (n 16-bit words) with one
+ * 16-byte store per 8 words, a wave's loads of 128 consecutive groups issued
+ * before their stores.  n a multiple of 8; b_bytes a multiple of 16; a
+ * 8-byte, b and out 16-byte aligned device pointers.  Grid: 3 workgroups of
+ * 512 threads per compute unit (the decode's), at most max_groups if
+ * nonzero.  The words written are a function of the bytes
+ * read, of no use beyond that.  Enqueued on hip_stream.  Errors: ARG, HIP. */
+int df11_stream_ceiling(const uint8_t *a, const uint8_t *b, uint64_t b_bytes, uint16_t *out,
+                        uint64_t n, uint32_t max_groups, void *hip_stream);
 
 #ifdef __cplusplus
 }

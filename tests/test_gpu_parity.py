@@ -96,17 +96,7 @@ def test_full_size_configs(torch, name):
     rng = np.random.default_rng(99)
     nb = int(enc.sizes.n_blocks)
     blocks = np.unique(np.concatenate([[0, nb - 1], rng.choice(nb, min(nb, 48), replace=False)]))
-    stop = int(enc.sizes.last_start) + 1
-    gbits = np.unpackbits(enc.gaps, bitorder="little")
-    for b in blocks.tolist():
-        p0, p1 = int(enc.block_pos[b]), int(enc.block_pos[b + 1])
-        g = 64 * b
-        gap = int(sum(int(gbits[5 * g + j]) << j for j in range(5)))
-        ex = oracle.decode_range(enc.stream, int(enc.sizes.total_bits), 4096 * b + gap,
-                                 min(4096 * (b + 1), stop), enc.codebook.lengths, 4096)
-        assert ex.size == p1 - p0
-        ref = oracle.join_bf16(ex, enc.signmant[p0:p1])
-        assert np.array_equal(got[p0:p1], ref), f"block {b}"
+    _oracle_blocks(enc, lambda p0, p1: got[p0:p1], blocks.tolist())
 
 
 @pytest.mark.parametrize("kind,n,seed", [("normal", 300_000, 31), ("single", 4096 * 40, 32),
@@ -285,6 +275,107 @@ def test_stack_pipeline_overlapped_matches_bf16_gemms(torch):
             for i in range(len(blocks)):
                 for sh in ref[i]:
                     assert torch.equal(outs[i][sh], ref[i][sh]), (mode, batch, i, sh)
+
+
+def _oracle_blocks(enc, fetch, blocks):
+    """The oracle decodes the given blocks of enc's stream on its own, from
+    each block's gap offset; each must equal the GPU output there
+    (fetch(p0, p1): the GPU's words p0..p1 as uint16)."""
+    stop = int(enc.sizes.last_start) + 1
+    gbits = np.unpackbits(enc.gaps, bitorder="little")
+    for b in blocks:
+        p0, p1 = int(enc.block_pos[b]), int(enc.block_pos[b + 1])
+        gap = int(sum(int(gbits[5 * 64 * b + j]) << j for j in range(5)))
+        ex = oracle.decode_range(enc.stream, int(enc.sizes.total_bits), 4096 * b + gap,
+                                 min(4096 * (b + 1), stop), enc.codebook.lengths, 4096)
+        assert ex.size == p1 - p0, f"block {b}"
+        assert np.array_equal(fetch(p0, p1), oracle.join_bf16(ex, enc.signmant[p0:p1])), f"block {b}"
+
+
+@pytest.mark.parametrize("layer", list(range(32)))
+def test_stack_block_full_size(torch, layer):
+    """The 32-block Llama-3.1-8B-shaped stack at full size, one block at a
+    time (218,103,808 weights each, seeds (3001, layer)): generate, encode,
+    decode, compare bit for bit with the originals on the GPU, and decode
+    sampled blocks with the oracle.  On the first and the last block the
+    consumer GEMMs (batch 1 and 64) on the decoded weights must equal those on
+    the originals, matrix by matrix."""
+    wlx = wl.llama8b_stack_block(layer)
+    enc = hd.encode(wlx.weights)
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    dev = hd.to_device(enc, status=st)
+    out = torch.full((enc.n + GUARD,), 0x5555, dtype=torch.int16, device="cuda")
+    _say(f"[gpu] df11_decode stack layer {layer} n={enc.n} blocks={enc.sizes.n_blocks}")
+    hd.df11_decode(dev, out)
+    orig = torch.from_numpy(wlx.weights.view(np.int16)).cuda()
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    assert bool((out[enc.n:] == 0x5555).all()), "write past the end of the tensor"
+    assert torch.equal(out[:enc.n], orig), f"layer {layer} differs from the original weights"
+    nb = int(enc.sizes.n_blocks)
+    rng = np.random.default_rng(layer)
+    sample = sorted(set([0, nb - 1] + rng.choice(nb, 6, replace=False).tolist()))
+    _oracle_blocks(enc, lambda p0, p1: out[p0:p1].cpu().numpy().view(np.uint16), sample)
+    if layer in (0, 31):
+        dec = out[:enc.n].view(torch.bfloat16)
+        ref = orig.view(torch.bfloat16)
+        gen = torch.Generator(device="cuda").manual_seed(3999)
+        off = 0
+        for m in wlx.matrices:
+            wd = dec[off: off + m.rows * m.cols].view(m.rows, m.cols)
+            wo = ref[off: off + m.rows * m.cols].view(m.rows, m.cols)
+            for batch in (1, 64):
+                x = torch.randn(batch, m.cols, generator=gen, device="cuda").to(torch.bfloat16)
+                _say(f"[gpu] stack layer {layer} GEMM {m.name} batch={batch}")
+                y0 = torch.matmul(x, wo.t())
+                y1 = torch.matmul(x, wd.t())
+                assert torch.equal(y0, y1), (layer, m.name, batch)
+            off += m.rows * m.cols
+    del out, orig, dev, enc
+
+
+@pytest.fixture(scope="module")
+def small_stack(torch):
+    from huffman_decode_amd.pipeline import StackBlock
+    blocks, originals = [], []
+    for layer in range(4):
+        w = wl.llama8b_block(seed=(3001, layer), scale=1 / 16)
+        enc = hd.encode(w.weights)
+        blocks.append(StackBlock(hd.to_device(enc), [(m.rows, m.cols) for m in w.matrices]))
+        originals.append(torch.from_numpy(w.weights.view(np.int16)).cuda().view(torch.bfloat16))
+    return blocks, originals
+
+
+@pytest.mark.parametrize("groups", [8, 256, 384, 512])
+def test_capped_decode_grid(torch, small_stack, groups):
+    """A decode grid capped at `groups` workgroups (df11_device_stream.max_groups,
+    what the overlapped schedule uses to leave compute units to the GEMMs)
+    decodes bit-exact, and the overlapped schedule with that cap gives the same
+    GEMM outputs as the GEMMs on the original weights."""
+    from huffman_decode_amd.pipeline import StackRunner
+    blocks, originals = small_stack
+    for i, (blk, orig) in enumerate(zip(blocks, originals)):
+        out = torch.full((blk.dev.n + GUARD,), 0x5555, dtype=torch.int16, device="cuda")
+        blk.dev.desc.max_groups = groups
+        _say(f"[gpu] df11_decode capped at {groups} groups, block {i}")
+        try:
+            hd.df11_decode(blk.dev, out)
+        finally:
+            blk.dev.desc.max_groups = 0
+        torch.cuda.synchronize()
+        assert torch.equal(out[:blk.dev.n], orig.view(torch.int16)), (groups, i)
+        assert bool((out[blk.dev.n:] == 0x5555).all())
+    runner = StackRunner(blocks)
+    for batch in (1, 64):
+        acts, ref = runner.activations(batch, per_block=True)
+        runner.run_gemms_only(acts, ref, originals)
+        _, outs = runner.activations(batch, per_block=True)
+        _say(f"[gpu] stack pipeline overlapped, decode capped at {groups}, batch={batch}")
+        runner.run_overlapped(acts, outs, groups)
+        torch.cuda.synchronize()
+        for i in range(len(blocks)):
+            for sh in ref[i]:
+                assert torch.equal(outs[i][sh], ref[i][sh]), (groups, batch, i, sh)
 
 
 # ---------------------------------------------------------------------------

@@ -314,8 +314,9 @@ def test_checksum_detects_a_flipped_bit_and_offload_refuses_it():
 
 def test_bench_reports_traffic_only_for_the_profiled_workload():
     """bench.py takes roofline.traffic from the committed counter profile only
-    when that profile was taken on the current kernel source and on the
-    workload being measured (same algorithmic bytes per launch)."""
+    when that profile was taken on the current kernel (the hash of its machine
+    code that the build records) and on the workload being measured (same
+    algorithmic bytes per launch)."""
     import importlib.util
     root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
     spec = importlib.util.spec_from_file_location("bench_mod", os.path.join(root, "bench.py"))
@@ -325,7 +326,39 @@ def test_bench_reports_traffic_only_for_the_profiled_workload():
     alg = int(re.search(r"^algorithmic_bytes_per_launch: (\d+)", text, re.M).group(1))
     assert bench.measured_traffic(alg + 1) is None
     got = bench.measured_traffic(alg)
-    if re.search(r"^kernel_sha256_16: (\w+)", text, re.M).group(1) == bench.kernel_hash():
+    if re.search(r"^kernel_isa_sha16: (\w+)", text, re.M).group(1) == bench.kernel_hash():
         assert got is not None and 0.95 * alg < got < 1.10 * alg
     else:
         assert got is None
+
+
+def test_fused_wrappers_check_x_and_y_before_any_launch():
+    """The C calls of the fused product receive no sizes for x and y, so the
+    binding checks them: x and y must reach every matrix's inputs and
+    results, and every tensor must sit on the encoded tensor's device.  All
+    of it fails before anything is launched (CPU tensors stand in here)."""
+    import torch
+    shapes = [(8, 2048), (4, 4096)]
+    w = wl.random_small(sum(r * c for r, c in shapes), 9, "normal")
+    dev = hd.to_device(hd.encode(w), "cpu")
+    mats, nx, ny = hd.gemv_matrices(shapes)
+    ws = torch.empty(hd.df11_gemv_workspace_bytes(dev), dtype=torch.uint8)
+    x = torch.zeros(nx, dtype=torch.bfloat16)
+    y = torch.zeros(ny, dtype=torch.float32)
+    with pytest.raises(ValueError, match="need"):
+        hd.df11_decode_gemv(dev, mats, x[: nx - 8], y, ws)
+    with pytest.raises(ValueError, match="need"):
+        hd.df11_decode_gemv(dev, mats, x, y[: ny - 1], ws)
+    with pytest.raises(ValueError, match="device"):
+        hd.df11_decode_gemv(dev, mats, x.to("meta"), y, ws)
+    with pytest.raises(ValueError, match="device"):
+        hd.df11_decode_gemv(dev, mats, x, y, ws.to("meta"))
+    xb = torch.zeros(3, nx, dtype=torch.bfloat16)
+    yb = torch.zeros(3, ny, dtype=torch.float32)
+    ws3 = torch.empty(hd.df11_gemm_workspace_bytes(dev, 3), dtype=torch.uint8)
+    with pytest.raises(ValueError, match="need"):
+        hd.df11_decode_gemm(dev, mats, xb[:, : nx - 8], yb, ws3)
+    with pytest.raises(ValueError, match="need"):
+        hd.df11_decode_gemm(dev, mats, xb, yb[:, : ny - 1], ws3)
+    with pytest.raises(ValueError, match="device"):
+        hd.df11_decode_gemm(dev, mats, xb, yb.to("meta"), ws3)
