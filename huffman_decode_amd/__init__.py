@@ -106,6 +106,10 @@ def _load():
             lib.df11_decode_gemm.argtypes = [ctypes.POINTER(DeviceStream), ctypes.POINTER(GemvMatrix),
                                              _U32, _P, _U32, _U64, _P, _U64, _P, _U64, _P]
             lib.df11_decode_gemm.restype = ctypes.c_int
+        lib.df11_decode_gemm_noalloc.argtypes = [ctypes.POINTER(DeviceStream),
+                                                 ctypes.POINTER(GemvMatrix), _U32, _P, _U32,
+                                                 _U64, _P, _U64, _P]
+        lib.df11_decode_gemm_noalloc.restype = ctypes.c_int
         lib.df11_stream_ceiling.argtypes = [_P, _P, _U64, _P, _U64, _U32, _P]
         lib.df11_stream_ceiling.restype = ctypes.c_int
         _lib = lib
@@ -360,12 +364,10 @@ def df11_gemm_workspace_bytes(dev: DeviceEncoded, batch: int) -> int:
     return int(_load().df11_gemm_workspace_bytes(ctypes.byref(dev.desc), batch))
 
 
-def df11_decode_gemm(dev: DeviceEncoded, mats: list[GemvMatrix], x, y, workspace,
-                     stream=None) -> None:
-    """Enqueue y[b] = W x[b] for every matrix of ``dev`` and every row b of x
-    (x a [batch, nx] bfloat16 and y a [batch, ny] float32 CUDA tensor, batch
-    1..8, rows strided by their row stride; workspace a CUDA tensor of at
-    least df11_gemm_workspace_bytes(dev, batch) bytes)."""
+def _check_gemm_xy(dev: DeviceEncoded, mats: list[GemvMatrix], x, y) -> None:
+    """x [batch, nx] bf16 and y [batch, ny] fp32 with unit column stride, on
+    the encoded tensor's device, reaching every matrix's inputs and results
+    (the C calls receive no sizes for them)."""
     import torch
     if x.dtype != torch.bfloat16 or x.dim() != 2 or x.stride(1) != 1:
         raise ValueError("x must be a [batch, nx] bfloat16 tensor with unit column stride")
@@ -373,11 +375,22 @@ def df11_decode_gemm(dev: DeviceEncoded, mats: list[GemvMatrix], x, y, workspace
         raise ValueError("y must be a [batch, ny] float32 tensor with unit column stride")
     if x.shape[0] != y.shape[0]:
         raise ValueError("x and y must hold the same number of vectors")
-    _same_device(dev, x=x, y=y, workspace=workspace)
+    _same_device(dev, x=x, y=y)
     x_end, y_end = _matrix_ends(mats)
     if x.shape[1] < x_end or y.shape[1] < y_end:
         raise ValueError(f"x rows hold {x.shape[1]} and y rows {y.shape[1]} elements; the "
                          f"matrices need {x_end} and {y_end}")
+
+
+def df11_decode_gemm(dev: DeviceEncoded, mats: list[GemvMatrix], x, y, workspace,
+                     stream=None) -> None:
+    """Enqueue y[b] = W x[b] for every matrix of ``dev`` and every row b of x
+    (x a [batch, nx] bfloat16 and y a [batch, ny] float32 CUDA tensor, batch
+    1..8, rows strided by their row stride; workspace a CUDA tensor of at
+    least df11_gemm_workspace_bytes(dev, batch) bytes)."""
+    import torch
+    _check_gemm_xy(dev, mats, x, y)
+    _same_device(dev, workspace=workspace)
     if stream is None:
         stream = torch.cuda.current_stream(y.device)
     arr = (GemvMatrix * len(mats))(*mats)
@@ -385,6 +398,24 @@ def df11_decode_gemm(dev: DeviceEncoded, mats: list[GemvMatrix], x, y, workspace
     _check("df11_decode_gemm", _load().df11_decode_gemm(
         ctypes.byref(dev.desc), arr, len(mats), x.data_ptr(), x.shape[0], x.stride(0),
         y.data_ptr(), y.stride(0), workspace.data_ptr(), nbytes, stream.cuda_stream))
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def df11_decode_gemm_noalloc(dev: DeviceEncoded, mats: list[GemvMatrix], x, y,
+                             stream=None) -> None:
+    """df11_decode_gemm without a workspace argument: the library's static
+    device array (NOALLOC_SCRATCH_BYTES per GPU) serves instead, and nothing
+    is allocated.  Calls that overlap on one GPU share that array and race."""
+    import torch
+    _check_gemm_xy(dev, mats, x, y)
+    if stream is None:
+        stream = torch.cuda.current_stream(y.device)
+    arr = (GemvMatrix * len(mats))(*mats)
+    _check("df11_decode_gemm_noalloc", _load().df11_decode_gemm_noalloc(
+        ctypes.byref(dev.desc), arr, len(mats), x.data_ptr(), x.shape[0], x.stride(0),
+        y.data_ptr(), y.stride(0), stream.cuda_stream))
 
 
 # ------------------------------------------------------------ measurement aid

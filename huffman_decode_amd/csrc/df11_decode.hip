@@ -1284,10 +1284,11 @@ static int launch_gemm(const df11_device_stream *s, const DecodeArgs &a, const G
     return hipGetLastError() == hipSuccess ? DF11_OK : DF11_ERR_HIP;
 }
 
-extern "C" int df11_decode_gemm(const df11_device_stream *s, const df11_gemv_matrix *mats,
-                                uint32_t n_mats, const uint16_t *x, uint32_t batch,
-                                uint64_t x_stride, float *y, uint64_t y_stride, void *workspace,
-                                uint64_t workspace_bytes, void *hip_stream) {
+// The fused product with its workspace given as a device address.
+static int decode_gemm(const df11_device_stream *s, const df11_gemv_matrix *mats, uint32_t n_mats,
+                       const uint16_t *x, uint32_t batch, uint64_t x_stride, float *y,
+                       uint64_t y_stride, void *workspace, uint64_t workspace_bytes,
+                       void *hip_stream) {
     if (!mats || !x || !y || !workspace) return DF11_ERR_ARG;
     DecodeArgs a;
     int st = prepare(s, nullptr, &a);
@@ -1343,8 +1344,50 @@ extern "C" int df11_decode_gemm(const df11_device_stream *s, const df11_gemv_mat
     }
 }
 
+extern "C" int df11_decode_gemm(const df11_device_stream *s, const df11_gemv_matrix *mats,
+                                uint32_t n_mats, const uint16_t *x, uint32_t batch,
+                                uint64_t x_stride, float *y, uint64_t y_stride, void *workspace,
+                                uint64_t workspace_bytes, void *hip_stream) {
+    return decode_gemm(s, mats, n_mats, x, batch, x_stride, y, y_stride, workspace,
+                       workspace_bytes, hip_stream);
+}
+
 extern "C" int df11_decode_gemv(const df11_device_stream *s, const df11_gemv_matrix *mats,
                                 uint32_t n_mats, const uint16_t *x, float *y, void *workspace,
                                 uint64_t workspace_bytes, void *hip_stream) {
-    return df11_decode_gemm(s, mats, n_mats, x, 1, 0, y, 0, workspace, workspace_bytes, hip_stream);
+    return decode_gemm(s, mats, n_mats, x, 1, 0, y, 0, workspace, workspace_bytes, hip_stream);
+}
+
+// ------------------------------------------------ the product without allocation
+//
+// The workspace of df11_decode_gemm_noalloc: one static device array, which
+// every GPU the library runs on holds (at its own address) until the process
+// ends.  Host code never names it directly (the name is a host-side stand-in):
+// its device address is taken once per device with hipGetSymbolAddress.
+static __device__ __align__(256) uint8_t scratch[DF11_NOALLOC_SCRATCH_BYTES];
+static std::atomic<void *> g_scratch[kMaxDevices];
+
+// scratch's address on the current device (`dev`), looked up on the first call
+// there; null if the runtime refuses
+static void *scratch_on(int dev) {
+    void *p = g_scratch[dev].load(std::memory_order_acquire);
+    if (p) return p;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    g_scratch[dev].store(p, std::memory_order_release);
+    return p;
+}
+
+extern "C" int df11_decode_gemm_noalloc(const df11_device_stream *s, const df11_gemv_matrix *mats,
+                                        uint32_t n_mats, const uint16_t *x, uint32_t batch,
+                                        uint64_t x_stride, float *y, uint64_t y_stride,
+                                        void *hip_stream) {
+    if (!s || batch < 1 || batch > (uint32_t)kGemmMaxBatch) return DF11_ERR_ARG;
+    const uint64_t need = df11_gemm_workspace_bytes(s, batch);
+    if (need > (uint64_t)DF11_NOALLOC_SCRATCH_BYTES) return DF11_ERR_BUFSIZE;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return DF11_ERR_HIP;
+    void *ws = scratch_on(dev);
+    if (!ws) return DF11_ERR_HIP;
+    return decode_gemm(s, mats, n_mats, x, batch, x_stride, y, y_stride, ws,
+                       (uint64_t)DF11_NOALLOC_SCRATCH_BYTES, hip_stream);
 }

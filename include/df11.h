@@ -248,6 +248,28 @@ int df11_decode_gemm(const df11_device_stream *s, const df11_gemv_matrix *mats, 
                      uint64_t y_stride, void *workspace, uint64_t workspace_bytes,
                      void *hip_stream);
 
+/* Workspace bytes df11_decode_gemm_noalloc can use (32 MiB): enough for
+ * batches 1-8 on the 218 M-weight Llama-3.1-8B-shaped block and batches 1-2 on
+ * the 856 M-weight Llama-3.3-70B-shaped block. */
+#define DF11_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+/* df11_decode_gemm for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, results and errors as df11_decode_gemm, without the
+ * workspace: the library's own static device array of
+ * DF11_NOALLOC_SCRATCH_BYTES serves instead (each GPU the library runs on
+ * holds one until the process ends; its address is looked up on the first
+ * call on each device).  It allocates nothing and frees nothing.  A stream
+ * and batch whose workspace (df11_gemm_workspace_bytes) exceeds that size is
+ * refused with BUFSIZE before any device call.  Every call on one GPU shares
+ * that GPU's array: calls that overlap on one GPU (other streams, other host
+ * threads) race and must be ordered by the caller.  Nothing in the array
+ * needs to start at zero: each call writes every entry it reads for intact
+ * blocks. */
+int df11_decode_gemm_noalloc(const df11_device_stream *s, const df11_gemv_matrix *mats,
+                             uint32_t n_mats, const uint16_t *x, uint32_t batch,
+                             uint64_t x_stride, float *y, uint64_t y_stride, void *hip_stream);
+
 /* ------------------------------------------------------- measurement aid */
 
 /* Streaming ceiling: a kernel that moves the bytes of one df11_decode launch

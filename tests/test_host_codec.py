@@ -362,3 +362,23 @@ def test_fused_wrappers_check_x_and_y_before_any_launch():
         hd.df11_decode_gemm(dev, mats, xb, yb[:, : ny - 1], ws3)
     with pytest.raises(ValueError, match="device"):
         hd.df11_decode_gemm(dev, mats, xb, yb.to("meta"), ws3)
+
+
+def test_noalloc_product_refuses_a_workspace_beyond_its_array():
+    """df11_decode_gemm_noalloc serves the workspace from a static device array
+    of NOALLOC_SCRATCH_BYTES; a stream and batch that need more are refused
+    with BUFSIZE before any device call (this runs without a GPU)."""
+    lib = hd.library()
+    d = hd.DeviceStream()
+    fake = 1 << 20
+    d.stream = d.gaps = d.block_pos = d.signmant = d.luts = fake
+    d.n = 855_638_016           # the 70B-shaped block
+    d.n_blocks = 540_000
+    mats = (hd.GemvMatrix * 1)(hd.GemvMatrix(0, 8192, d.n // 8192, 0, 0))
+    for batch in (4, 8):
+        need = lib.df11_gemm_workspace_bytes(ctypes.byref(d), batch)
+        assert need > hd.NOALLOC_SCRATCH_BYTES
+        assert lib.df11_decode_gemm_noalloc(ctypes.byref(d), mats, 1, fake, batch, 1 << 20,
+                                            fake, 8192, None) == -2
+    assert lib.df11_decode_gemm_noalloc(ctypes.byref(d), mats, 1, fake, 9, 1 << 20, fake, 8192,
+                                        None) == -1
