@@ -175,7 +175,7 @@ def run_copy(args) -> int:
     return 0
 
 
-def gemm_ratios(wlx, out, decode_ms, stream, batches=(1, 2, 4, 64), reps=10) -> dict:
+def gemm_ratios(wlx, out, decode_ms, stream, batches=(1, 2, 4, 16, 64), reps=10) -> dict:
     """Decode time of the block over the time of the block's bf16 GEMMs
     (y = x W^T for each of its matrices, on the decoded weights) at each batch."""
     import torch
@@ -370,6 +370,40 @@ def fused_gemm(wlx, copies, stream, batch, reps=20) -> dict:
     b.record(stream)
     torch.cuda.synchronize()
     return {"fused_ms": round(a.elapsed_time(b) / reps, 5)}
+
+
+def fused_tiled(wlx, stream, batches, n_copies=3, reps=20) -> dict:
+    """y_b = W x_b for `batch` vectors on the matrix cores from the block
+    encoded in operand-tile order (df11_decode_gemm_tiled), timed over
+    back-to-back launches on rotating copies like the decode."""
+    import numpy as np
+    import torch
+    import huffman_decode_amd as hd
+    shapes = [(m.rows, m.cols) for m in wlx.matrices]
+    te = hd.encode_tiled(wlx.weights, shapes)
+    copies = [hd.tiled_to_device(te, "cuda") for _ in range(n_copies)]
+    nx = max(m.x_offset + m.cols for m in te.mats)
+    ny = sum(m.rows for m in te.mats)
+    rd, _ = algorithmic_bytes(te.enc)
+    res = {}
+    for batch in batches:
+        x = torch.from_numpy(np.random.default_rng(9).standard_normal((batch, nx)).astype(np.float32))
+        x = x.cuda().to(torch.bfloat16)
+        y = torch.empty(batch, ny, dtype=torch.float32, device="cuda")
+        for k in range(3):
+            hd.df11_decode_gemm_tiled(copies[k % n_copies], x, y, stream)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for k in range(reps):
+            hd.df11_decode_gemm_tiled(copies[k % n_copies], x, y, stream)
+        b.record(stream)
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / reps
+        res[f"batch{batch}"] = {"fused_ms": round(ms, 5),
+                                "fused_gbs": round((rd + 2 * batch * nx + 4 * batch * ny)
+                                                   / (ms * 1e-3) / 1e9, 1)}
+    return res
 
 
 def run_offload(args) -> int:
@@ -614,6 +648,13 @@ def main() -> int:
             f["fused_gbs"] = round((rd + 2 * b * nx + 4 * b * ny) / (f["fused_ms"] * 1e-3) / 1e9, 1)
             fused[f"batch{b}"] = f
         line["decode_vs_gemm"]["fused"] = fused
+        # the tiled product on the matrix cores (its own tile-order encoding)
+        tiled = fused_tiled(wlx, stream, (1, 16, 64))
+        for key, f in tiled.items():
+            g = line["decode_vs_gemm"][key]["gemm_ms"]
+            f["over_bf16_gemm"] = round(f["fused_ms"] / g, 4)
+            f["over_decode_then_gemm"] = round(f["fused_ms"] / (avg_ms + g), 4)
+        line["decode_vs_gemm"]["fused_tiled"] = tiled
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wlx, enc)
     print(json.dumps(line), flush=True)

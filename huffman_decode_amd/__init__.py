@@ -110,6 +110,16 @@ def _load():
                                                  ctypes.POINTER(GemvMatrix), _U32, _P, _U32,
                                                  _U64, _P, _U64, _P]
         lib.df11_decode_gemm_noalloc.restype = ctypes.c_int
+        lib.df11_tile_order.argtypes = [_P, _U64, ctypes.POINTER(GemvMatrix), _U32, _P, _U32]
+        lib.df11_tile_order.restype = ctypes.c_int
+        lib.df11_tile_segment_count.argtypes = [ctypes.POINTER(GemvMatrix), _U32]
+        lib.df11_tile_segment_count.restype = _U64
+        lib.df11_tile_segments.argtypes = [_P, _U32, ctypes.POINTER(GemvMatrix), _U32, _P, _U64]
+        lib.df11_tile_segments.restype = ctypes.c_int
+        lib.df11_decode_gemm_tiled.argtypes = [ctypes.POINTER(DeviceStream),
+                                               ctypes.POINTER(GemvMatrix), _U32, _P, _P, _U32,
+                                               _U64, _P, _U64, _P]
+        lib.df11_decode_gemm_tiled.restype = ctypes.c_int
         lib.df11_stream_ceiling.argtypes = [_P, _P, _U64, _P, _U64, _U32, _P]
         lib.df11_stream_ceiling.restype = ctypes.c_int
         _lib = lib
@@ -416,6 +426,83 @@ def df11_decode_gemm_noalloc(dev: DeviceEncoded, mats: list[GemvMatrix], x, y,
     _check("df11_decode_gemm_noalloc", _load().df11_decode_gemm_noalloc(
         ctypes.byref(dev.desc), arr, len(mats), x.data_ptr(), x.shape[0], x.stride(0),
         y.data_ptr(), y.stride(0), stream.cuda_stream))
+
+
+# ------------------------------------------------------------ tiled product
+
+TILED_MAX_BATCH = 64
+
+
+def _mat_array(mats):
+    return (GemvMatrix * len(mats))(*mats)
+
+
+def df11_tile_order(w: np.ndarray, mats: list[GemvMatrix], n_threads: int = 0) -> np.ndarray:
+    """Row-major matrices laid end to end -> the same words in operand-tile
+    order (see include/df11.h); host only."""
+    w = np.ascontiguousarray(w, dtype=np.uint16).reshape(-1)
+    out = np.empty_like(w)
+    _check("df11_tile_order", _load().df11_tile_order(_ptr(w), w.size, _mat_array(mats), len(mats),
+                                                      _ptr(out), n_threads))
+    return out
+
+
+def df11_tile_segments(block_pos: np.ndarray, mats: list[GemvMatrix]) -> np.ndarray:
+    """First block of each 16-row segment, then the block of the last weight."""
+    bp = np.ascontiguousarray(block_pos, dtype=np.uint32)
+    arr = _mat_array(mats)
+    count = int(_load().df11_tile_segment_count(arr, len(mats)))
+    seg = np.zeros(count + 1, np.uint32)
+    _check("df11_tile_segments", _load().df11_tile_segments(_ptr(bp), bp.size - 1, arr, len(mats),
+                                                            _ptr(seg), seg.size))
+    return seg
+
+
+@dataclass
+class TiledEncoded:
+    """A block of matrices encoded in operand-tile order for the tiled
+    product: the encoded arrays, the matrix list and the segment table."""
+    enc: Encoded
+    mats: list
+    seg_blk: np.ndarray
+
+
+def encode_tiled(bf16: np.ndarray, shapes: list[tuple[int, int]], max_code_len: int = MAX_CODE_LEN,
+                 n_threads: int = 0) -> TiledEncoded:
+    """Row-major [rows, cols] matrices laid end to end (rows multiples of 16,
+    cols of 32) -> tile order -> DF11 arrays, plus the segment table."""
+    mats, _, _ = gemv_matrices(shapes)
+    tiled = df11_tile_order(bf16, mats, n_threads)
+    enc = encode(tiled, max_code_len, n_threads)
+    return TiledEncoded(enc, mats, df11_tile_segments(enc.block_pos, mats))
+
+
+@dataclass
+class TiledDevice:
+    dev: DeviceEncoded
+    mats: list
+    seg_blk: object  # device tensor (int32 view of the uint32 table)
+
+
+def tiled_to_device(te: TiledEncoded, device="cuda", status=None) -> TiledDevice:
+    import torch
+    dev = to_device(te.enc, device, status)
+    seg = torch.from_numpy(te.seg_blk.view(np.int32)).to(device)
+    return TiledDevice(dev, te.mats, seg)
+
+
+def df11_decode_gemm_tiled(td: TiledDevice, x, y, stream=None) -> None:
+    """Enqueue y[b] = W x[b] for every matrix and every row b of x (batch
+    1..64) from a tile-order stream, on the matrix cores (x [batch, nx]
+    bfloat16, y [batch, ny] float32, unit column stride; no workspace)."""
+    import torch
+    _check_gemm_xy(td.dev, td.mats, x, y)
+    _same_device(td.dev, seg_blk=td.seg_blk)
+    if stream is None:
+        stream = torch.cuda.current_stream(y.device)
+    _check("df11_decode_gemm_tiled", _load().df11_decode_gemm_tiled(
+        ctypes.byref(td.dev.desc), _mat_array(td.mats), len(td.mats), td.seg_blk.data_ptr(),
+        x.data_ptr(), x.shape[0], x.stride(0), y.data_ptr(), y.stride(0), stream.cuda_stream))
 
 
 # ------------------------------------------------------------ measurement aid

@@ -47,6 +47,7 @@
 //    contiguous range per XCD put eight write fronts in step and was slower.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cstring>
 #include <type_traits>
@@ -1143,6 +1144,325 @@ __global__ __launch_bounds__(256) void df11_gemm_reduce_kernel(GemvArgs g, uint3
         if ((uint32_t)b < g.batch) g.y[b * g.y_stride + yoff_m + r] = sum[b];
 }
 
+// ------------------------------------------------------------ tiled product
+//
+// y_b = W x_b for 1-64 vectors on the matrix cores, from a stream whose
+// weights are in operand-tile order (df11_tile_order): per matrix, row tiles
+// of 16 rows, then k-steps of 32 columns, then for each lane L of a
+// v_mfma_f32_16x16x32_bf16 the 8 weights W[16 rt + L % 16][32 ks + 8 (L / 16)
+// + 0..7].  So 512 consecutive decoded words are one operand tile A, and the
+// lane that takes group L of a tile from the LDS exponent tile holds exactly
+// its part of A.  (Row tiles of 32 rows, whose two halves share each k-step's
+// inputs, halve the bytes of x read but were slower overall: half as many
+// workgroups left more of them to a last, partly filled round.)
+//
+// One workgroup per segment (the 16 rows of one row tile); its waves take the
+// segment's blocks in turn (blk_lo + wave + 8 i: a fixed assignment, so sums
+// are formed in the same order on every run), decode each block into the
+// wave's LDS tile as the plain decode does, and multiply every operand tile
+// the block holds with the 32 x 16 slabs of x for each group of 16 vectors,
+// accumulating in registers (words outside the block or the segment are zero
+// in A).  At the end the waves' sums are added in LDS in wave order and the
+// workgroup writes its 16 results per vector.  Segments of the widest
+// matrices are launched first, so that the longest workgroups start early.
+constexpr int kTiledMaxBatch = 64;
+
+struct TiledArgs {
+    const uint16_t *x;        // matrix m's inputs at x + xoff; vector b at + b * x_stride
+    float *y;                 // matrix m's results at y + yoff; vector b at + b * y_stride
+    const uint32_t *seg_blk;  // per segment (matrix order) its first block; then the last block
+    uint64_t x_stride, y_stride;
+    uint32_t batch, n_mats;
+    // per launch-order entry e (matrices by decreasing cols): its first
+    // segment in launch order (first[n_mats] = number of segments), the
+    // matrix's first operand tile (offset / 512), k-steps (cols / 32),
+    // the matrix-order index of its first segment, and its x and y offsets
+    uint32_t first[kGemvMaxMats + 1];
+    uint32_t tile0[kGemvMaxMats];
+    uint32_t ksteps[kGemvMaxMats];
+    uint32_t seg0[kGemvMaxMats];
+    uint32_t xoff[kGemvMaxMats];
+    uint32_t yoff[kGemvMaxMats];
+};
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+
+// One lane's inputs for one block: its stream dwords, its gap dwords and
+// (even lanes) block_pos[blk] or (odd lanes) block_pos[blk + 1].
+struct BlockIn {
+    uint32_t d0, d1, d2, g0, g1, pos;
+};
+
+__device__ __forceinline__ BlockIn load_block(const DecodeArgs &a, uint32_t blk, uint32_t lane) {
+    BlockIn r;
+    const uint32_t *sp = a.stream + 2 * (blk * DF11_BLOCK_SLICES + lane);
+    r.d0 = sp[0], r.d1 = sp[1], r.d2 = sp[2];
+    const uint32_t *gp = a.gaps + 10 * blk + ((5 * lane) >> 5);
+    r.g0 = gp[0], r.g1 = gp[1];
+    r.pos = a.block_pos[blk + (lane & 1)];
+    return r;
+}
+
+// The lane's 8 sign|mantissa bytes of operand tile tt, if its group holds a
+// word of [w_lo, w_hi) (zero otherwise, and nothing is read).
+__device__ __forceinline__ uint2 tile_sm(const uint8_t *signmant, uint32_t tt, uint32_t w_lo,
+                                         uint32_t w_hi, uint32_t lane) {
+    const uint32_t q = (tt << 9) + 8 * lane;
+    return q + 8 > w_lo && q < w_hi ? load_sm8(signmant + q) : make_uint2(0, 0);
+}
+
+// Where the lane's B operands come from: vector 16 nt + lane % 16 of the
+// batch, inputs xl + 16 nt x_stride + 32 ks + 0..7 for k-step ks (xl already
+// holds the lane's vector, the matrix's x offset and the lane's 8 columns).
+struct XSrc {
+    const g_cu16 *xl;
+    uint64_t group_stride;  // 16 x_stride: from one group of 16 vectors to the next
+    uint32_t live;          // vectors of the lane's column below the batch: bit nt
+};
+
+// The lane's B operands of k-step ks: 8 inputs of vector 16 nt + lane % 16.
+template <int NT>
+__device__ __forceinline__ void tile_x(u32x4 (&bv)[NT], const XSrc &xs, uint32_t ks) {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+        bv[nt] = (xs.live >> nt) & 1u
+                     ? *(const g_cu32x4 *)(xs.xl + nt * xs.group_stride + 32 * ks)
+                     : u32x4{0, 0, 0, 0};
+}
+
+// The lane's A operand of operand tile tt: its 8 words (exponents at LDS tile
+// byte q - t_base, sign|mantissa bytes sm), those outside [w_lo, w_hi) zero.
+__device__ __forceinline__ u32x4 tile_a(const uint8_t *tile, uint32_t t_base, uint2 sm, uint32_t tt,
+                                        uint32_t w_lo, uint32_t w_hi, uint32_t lane) {
+    const uint32_t q = (tt << 9) + 8 * lane;
+    const uint32_t lo = q > w_lo ? q : w_lo, hi = q + 8 < w_hi ? q + 8 : w_hi;
+    u32x4 av = {0, 0, 0, 0};
+    if (lo < hi) {
+        const uint4 w = join8(*reinterpret_cast<const uint2 *>(tile + (q - t_base)), sm);
+        av = u32x4{w.x, w.y, w.z, w.w};
+        if (hi - lo < 8) {
+            const uint32_t a0 = lo - q, a1 = hi - q;  // words [a0, a1) are kept
+            auto keep = [&](uint32_t j) { return j >= a0 && j < a1; };
+            av.x &= (keep(0) ? 0xFFFFu : 0u) | (keep(1) ? 0xFFFF0000u : 0u);
+            av.y &= (keep(2) ? 0xFFFFu : 0u) | (keep(3) ? 0xFFFF0000u : 0u);
+            av.z &= (keep(4) ? 0xFFFFu : 0u) | (keep(5) ? 0xFFFF0000u : 0u);
+            av.w &= (keep(6) ? 0xFFFFu : 0u) | (keep(7) ? 0xFFFF0000u : 0u);
+        }
+    }
+    return av;
+}
+
+template <int NT>
+__device__ __forceinline__ void tile_mfma(f32x4 (&acc)[NT], u32x4 av, const u32x4 (&bv)[NT]) {
+    const bf16x8_t a8 = __builtin_bit_cast(bf16x8_t, av);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+        acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a8, __builtin_bit_cast(bf16x8_t, bv[nt]),
+                                                          acc[nt], 0, 0, 0);
+}
+
+// Multiply the operand tiles that words [w_lo, w_hi) of the decoded block
+// reach (each word's exponent at LDS tile byte q - t_base) into acc.
+template <int NT>
+__device__ __forceinline__ void mfma_window(uint32_t w_lo, uint32_t w_hi, uint32_t t_base,
+                                            const uint8_t *tile, const uint8_t *signmant,
+                                            const XSrc &xs, uint32_t seg_tile, uint32_t lane,
+                                            f32x4 (&acc)[NT]) {
+    for (uint32_t tt = w_lo >> 9; tt < (w_hi + 511) >> 9; ++tt) {
+        u32x4 bv[NT];
+        tile_x<NT>(bv, xs, tt - seg_tile);
+        const uint2 sm = tile_sm(signmant, tt, w_lo, w_hi, lane);
+        tile_mfma<NT>(acc, tile_a(tile, t_base, sm, tt, w_lo, w_hi, lane), bv);
+    }
+}
+
+// Occupancy: up to 32 vectors the decode's 80-VGPR budget (3 workgroups per
+// CU); 64 vectors 128 VGPRs (2 per CU).
+template <int NT> struct TiledOccupancy {
+    static constexpr int kValue = NT <= 2 ? kWavesPerEu : 4;
+};
+
+template <int NT>
+__global__ __launch_bounds__(kGroupThreads)
+__attribute__((amdgpu_waves_per_eu(TiledOccupancy<NT>::kValue)))
+void df11_tiled_kernel(DecodeArgs a, TiledArgs t) {
+    __shared__ __attribute__((aligned(16))) uint8_t lds_static[kStaticLds];
+    static_assert(8 * 4 * 256 * 4 <= kStaticLds, "the final sums of 8 waves fit the static LDS");
+    extern __shared__ uint4 smem_u4[];
+    uint16_t *lut = reinterpret_cast<uint16_t *>(smem_u4);
+    uint8_t *tiles = lds_static;
+    const uint8_t *lds_dec = lds_static + kTilesBytes;
+    if (lds_offset(tiles) + kTilesBytes > 0x10000u) {
+        if (threadIdx.x == 0 && a.status) atomicAdd(a.status, 1u);
+        return;
+    }
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const uint32_t lane = threadIdx.x % kWave;
+    uint8_t *tile = tiles + wave * kTileBytes;
+    const uint32_t tile_addr = lds_offset(tile);
+
+    // this workgroup's segment: row tile rt of launch-order entry e (fields
+    // taken with constant indices: a run-time index into the kernel argument
+    // would copy it to scratch memory)
+    const uint32_t k = blockIdx.x;
+    uint32_t e = 0;
+#pragma unroll
+    for (int i = 1; i < kGemvMaxMats; ++i) e += ((uint32_t)i < t.n_mats && k >= t.first[i]) ? 1u : 0u;
+    uint32_t first_e = 0, tile0_e = 0, ks_e = 0, seg0_e = 0, xoff_e = 0, yoff_e = 0;
+#pragma unroll
+    for (int i = 0; i < kGemvMaxMats; ++i)
+        if ((uint32_t)i == e) {
+            first_e = t.first[i], tile0_e = t.tile0[i], ks_e = t.ksteps[i];
+            seg0_e = t.seg0[i], xoff_e = t.xoff[i], yoff_e = t.yoff[i];
+        }
+    const uint32_t rt = k - first_e;
+    const uint32_t seg_tile = tile0_e + rt * ks_e;  // the segment's first operand tile
+    const uint32_t seg_lo = seg_tile << 9, seg_hi = seg_lo + (ks_e << 9);
+    const uint32_t seg = seg0_e + rt;
+    const uint32_t blk_lo = t.seg_blk[seg];
+    uint32_t blk_hi = t.seg_blk[seg + 1];
+    blk_hi = blk_hi < a.n_blocks ? blk_hi : a.n_blocks - 1;
+
+    // the lane's B operand: vector 16 nt + lane % 16, columns 8 (lane / 16)
+    // + 0..7 of each 32-column slab
+    XSrc xs;
+    xs.xl = (const g_cu16 *)t.x + (uint64_t)(lane % 16) * t.x_stride + xoff_e + 8 * (lane / 16);
+    xs.group_stride = 16 * t.x_stride;
+    xs.live = 0;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) xs.live |= (16 * nt + lane % 16 < t.batch ? 1u : 0u) << nt;
+
+    // tables into LDS while the wave's first block loads
+    const uint32_t hier_bytes = a.n_tables * kTableBytes;
+    const uint32_t lut_u4_count = hier_bytes / 16;
+    const bool lut_one_load = lut_u4_count <= kGroupThreads;
+    uint4 lv = {0, 0, 0, 0};
+    if (lut_one_load && threadIdx.x < lut_u4_count) lv = a.luts[threadIdx.x];
+    const uint4 *dec_src = a.luts + lut_u4_count;
+    const uint4 dv0 = dec_src[threadIdx.x], dv1 = dec_src[threadIdx.x + kGroupThreads];
+    uint32_t b = blk_lo + wave;
+    BlockIn nxt = load_block(a, b <= blk_hi ? b : blk_hi, lane);
+    uint4 *lut_u4 = reinterpret_cast<uint4 *>(lut);
+    if (lut_one_load) {
+        if (threadIdx.x < lut_u4_count) lut_u4[threadIdx.x] = lv;
+    } else {
+        for (uint32_t i = threadIdx.x; i < lut_u4_count; i += kGroupThreads) lut_u4[i] = a.luts[i];
+    }
+    reinterpret_cast<uint4 *>(lds_static + kTilesBytes)[threadIdx.x] = dv0;
+    reinterpret_cast<uint4 *>(lds_static + kTilesBytes)[threadIdx.x + kGroupThreads] = dv1;
+    group_lds_sync();
+
+    f32x4 acc[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    const uint32_t gap_shift = (5 * lane) & 31;
+    for (; b <= blk_hi; b += kWavesPerGroup) {
+        const BlockIn cur = nxt;
+        if (b + kWavesPerGroup <= blk_hi) nxt = load_block(a, b + kWavesPerGroup, lane);
+        const uint32_t p0 = __builtin_amdgcn_readlane(cur.pos, 0);
+        const uint32_t p1 = __builtin_amdgcn_readlane(cur.pos, 1);
+        const bool sane = p1 >= p0 && p1 <= a.n && p1 - p0 <= (uint32_t)kMaxBlockCodes;
+        const uint32_t base = p0 & ~7u;
+        const uint32_t groups = sane ? (p1 - base + 7) >> 3 : 0u;
+        const bool one_pass = groups * 8 + 4 <= (uint32_t)kTileCap;
+        // the block's words in this segment
+        const uint32_t w_lo = p0 > seg_lo ? p0 : seg_lo, w_hi = p1 < seg_hi ? p1 : seg_hi;
+        const uint32_t gw = __builtin_amdgcn_alignbit(cur.g1, cur.g0, gap_shift);
+        const uint32_t gap = gw & 31u, gap_next = (gw >> 5) & 31u;
+        // stop bit and stream end relative to this lane's slice (as in the decode)
+        auto from_block = [&](uint32_t blk, uint32_t rem) {
+            const int32_t d = (int32_t)(blk - b);
+            return d > 1 ? (1 << 30) : (d < -1 ? -(1 << 30) : d * 4096 + (int32_t)rem);
+        };
+        const int32_t stop_at = from_block(a.stop_blk, a.stop_rem);
+        uint32_t lim, f0, f1, f2;
+        if (stop_at > kWave * DF11_SLICE_BITS) {
+            lim = 64u;
+            f0 = cur.d0;
+            f1 = cur.d1;
+            f2 = cur.d2 | (0xFFFFFFFFu << gap_next);
+        } else {
+            const int32_t lane_bit = (int32_t)(lane * DF11_SLICE_BITS);
+            const int32_t rel = stop_at - lane_bit;
+            lim = rel <= 0 ? 0u : (rel >= 64 ? 64u : (uint32_t)rel);
+            const uint32_t end = rel > 0 && rel <= 64
+                                     ? (uint32_t)(from_block(a.end_blk, a.end_rem) - lane_bit)
+                                     : 64u + gap_next;
+            f0 = pad_ones(cur.d0, (int)end, 0);
+            f1 = pad_ones(cur.d1, (int)end, 32);
+            f2 = pad_ones(cur.d2, (int)end, 64);
+        }
+        // phase 1, scan
+        const uint32_t slot = tile_addr + kStageBase + lane * kStageStride;
+        const uint32_t cnt = lim ? stage_codes(lds_dec, lut, a.n_tables, cur.d0, cur.d1, cur.d2, f0,
+                                               f1, f2, gap, lim, slot)
+                                 : 0u;
+        const uint32_t incl = wave_inclusive_sum(cnt);
+        const uint32_t excl = incl - cnt;
+        const uint32_t total = __builtin_amdgcn_readlane(incl, kWave - 1);
+        if (!sane || total != p1 - p0) {  // a corrupt block: reported, its words left out
+            if (lane == 0 && a.status) atomicAdd(a.status, 1u);
+            wave_lds_sync();
+            continue;
+        }
+        const uint32_t at = (p0 - base) + excl;
+        const uint32_t start = lim ? gap : 0u;
+        const bool last_lane = incl == total;
+        const bool odd = cnt > (uint32_t)kStageCodes || (cnt < (uint32_t)kStageMinCodes && !last_lane);
+        const bool staged = one_pass && __builtin_amdgcn_ballot_w64(odd) == 0;
+        wave_lds_sync();
+        if (staged) {
+            const uint32_t tail = staged_tail(slot, cnt);
+            const uint32_t prev = (uint32_t)__builtin_amdgcn_ds_bpermute(
+                (int)(((lane + kWave - 1) % kWave) * 4), (int)tail);
+            place_staged(slot, tile_addr + at, cnt, prev, last_lane);
+            wave_lds_sync();
+        } else if (one_pass) {
+            decode_codes<false>(lds_dec, lut, a.n_tables, cur.d0, cur.d1, cur.d2, start, lim,
+                                tile_addr, at, 0);
+            wave_lds_sync();
+            rewrite_head(lds_dec, lut, a.n_tables, cur.d0, cur.d1, cur.d2, start, cnt,
+                         tile_addr + at);
+            wave_lds_sync();
+        }
+        if (one_pass) {
+            if (w_lo < w_hi)
+                mfma_window<NT>(w_lo, w_hi, base, tile, a.signmant, xs, seg_tile, lane, acc);
+            wave_lds_sync();
+        } else {
+            // more symbols than one tile holds: decode again per tile-sized window
+            for (uint32_t r0 = 0; r0 < groups * 8; r0 += kTileCap) {
+                decode_codes<true>(lds_dec, lut, a.n_tables, cur.d0, cur.d1, cur.d2, start, lim,
+                                   tile_addr, at, r0);
+                wave_lds_sync();
+                const uint32_t r_lo = base + r0, r_hi = base + r0 + kTileCap;
+                const uint32_t v_lo = w_lo > r_lo ? w_lo : r_lo, v_hi = w_hi < r_hi ? w_hi : r_hi;
+                if (v_lo < v_hi)
+                    mfma_window<NT>(v_lo, v_hi, r_lo, tile, a.signmant, xs, seg_tile, lane, acc);
+                wave_lds_sync();
+            }
+        }
+    }
+
+    // every wave's blocks are done and the LDS is free: sum the waves' 16 x 16
+    // results per group of vectors in wave order and write them
+    group_lds_sync();
+    float *red = reinterpret_cast<float *>(lds_static);  // [wave][nt][lane][4]
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+        *reinterpret_cast<f32x4 *>(red + ((wave * NT + nt) * kWave + lane) * 4) = acc[nt];
+    group_lds_sync();
+    for (uint32_t o = threadIdx.x; o < (uint32_t)NT * 256; o += kGroupThreads) {
+        const uint32_t nt = o / 256, j = (o % 256) / 16, i = o % 16;  // vector 16 nt + j, row i
+        const uint32_t src = (j + 16 * (i / 4)) * 4 + i % 4;           // D[i][j]: lane, register
+        float sum = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kWavesPerGroup; ++w) sum += red[(w * NT + nt) * 256 + src];
+        const uint32_t vb = 16 * nt + j;
+        if (vb < t.batch) t.y[(uint64_t)vb * t.y_stride + yoff_e + 16 * rt + i] = sum;
+    }
+}
+
 // Launch shape per device: compute units and, per kernel, resident
 // workgroups per CU for each table count (the LDS footprint depends on it).
 constexpr int kMaxDevices = 16;
@@ -1390,4 +1710,72 @@ extern "C" int df11_decode_gemm_noalloc(const df11_device_stream *s, const df11_
     if (!ws) return DF11_ERR_HIP;
     return decode_gemm(s, mats, n_mats, x, batch, x_stride, y, y_stride, ws,
                        (uint64_t)DF11_NOALLOC_SCRATCH_BYTES, hip_stream);
+}
+
+
+// ------------------------------------------------------------ tiled product launch
+
+extern "C" int df11_decode_gemm_tiled(const df11_device_stream *s, const df11_gemv_matrix *mats,
+                                      uint32_t n_mats, const uint32_t *seg_blk, const uint16_t *x,
+                                      uint32_t batch, uint64_t x_stride, float *y,
+                                      uint64_t y_stride, void *hip_stream) {
+    if (!mats || !seg_blk || !x || !y) return DF11_ERR_ARG;
+    DecodeArgs a;
+    int st = prepare(s, nullptr, &a);
+    if (st != DF11_OK) return st;
+    if (n_mats < 1 || n_mats > (uint32_t)kGemvMaxMats || batch < 1 ||
+        batch > (uint32_t)kTiledMaxBatch || !aligned(x, 16) || !aligned(y, 4) || !aligned(seg_blk, 4))
+        return DF11_ERR_ARG;
+    if (batch > 1 && (x_stride % 8 != 0 || x_stride >= (1ull << 32) || y_stride >= (1ull << 32)))
+        return DF11_ERR_ARG;
+    uint64_t off = 0, segs = 0, x_end = 0, y_end = 0;
+    uint32_t seg0[kGemvMaxMats];
+    for (uint32_t m = 0; m < n_mats; ++m) {
+        const df11_gemv_matrix &mm = mats[m];
+        if (mm.offset != off || mm.rows == 0 || mm.rows % 16 != 0 || mm.cols == 0 ||
+            mm.cols % 32 != 0 || mm.x_offset % 8 != 0)
+            return DF11_ERR_ARG;
+        seg0[m] = (uint32_t)segs;
+        off += (uint64_t)mm.rows * mm.cols;
+        segs += mm.rows / 16;
+        const uint64_t xe = (uint64_t)mm.x_offset + mm.cols, ye = (uint64_t)mm.y_offset + mm.rows;
+        x_end = xe > x_end ? xe : x_end;
+        y_end = ye > y_end ? ye : y_end;
+        if (off > s->n || ye >= (1ull << 32)) return DF11_ERR_ARG;
+    }
+    if (off != s->n) return DF11_ERR_ARG;
+    if (batch > 1 && (x_stride < x_end || y_stride < y_end)) return DF11_ERR_ARG;
+    // launch order: matrices by decreasing cols (their segments take longest)
+    uint32_t order[kGemvMaxMats];
+    for (uint32_t m = 0; m < n_mats; ++m) order[m] = m;
+    std::stable_sort(order, order + n_mats,
+                     [&](uint32_t p, uint32_t q) { return mats[p].cols > mats[q].cols; });
+    TiledArgs t;
+    std::memset(&t, 0, sizeof(t));
+    t.x = x;
+    t.y = y;
+    t.seg_blk = seg_blk;
+    t.x_stride = batch > 1 ? x_stride : 0;
+    t.y_stride = batch > 1 ? y_stride : 0;
+    t.batch = batch;
+    t.n_mats = n_mats;
+    uint32_t run = 0;
+    for (uint32_t e = 0; e < n_mats; ++e) {
+        const df11_gemv_matrix &mm = mats[order[e]];
+        t.first[e] = run;
+        t.tile0[e] = (uint32_t)(mm.offset / 512);
+        t.ksteps[e] = mm.cols / 32;
+        t.seg0[e] = seg0[order[e]];
+        t.xoff[e] = mm.x_offset;
+        t.yoff[e] = mm.y_offset;
+        run += mm.rows / 16;
+    }
+    t.first[n_mats] = run;
+    const hipStream_t hs = static_cast<hipStream_t>(hip_stream);
+    const dim3 grid(run), block(kGroupThreads);
+    const size_t lds = lds_bytes(s->n_tables);
+    if (batch <= 16) hipLaunchKernelGGL(df11_tiled_kernel<1>, grid, block, lds, hs, a, t);
+    else if (batch <= 32) hipLaunchKernelGGL(df11_tiled_kernel<2>, grid, block, lds, hs, a, t);
+    else hipLaunchKernelGGL(df11_tiled_kernel<4>, grid, block, lds, hs, a, t);
+    return hipGetLastError() == hipSuccess ? DF11_OK : DF11_ERR_HIP;
 }

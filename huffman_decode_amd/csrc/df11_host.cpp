@@ -460,3 +460,86 @@ extern "C" int df11_encode(const uint16_t *bf16, uint64_t n, const df11_codebook
     out->lut_bytes = df11_internal::lut_image_bytes(cb->n_tables);
     return DF11_OK;
 }
+
+// ------------------------------------------------ layout for the tiled product
+//
+// The tiled fused product multiplies 16-row tiles of a matrix with up to 64
+// input vectors on the matrix cores.  Its weights are stored in the order in
+// which a 16x16x32 bf16 matrix instruction takes its first operand, so that
+// the decoded words come out of a block already in operand order: per matrix,
+// row tiles rt (16 rows), then k-steps ks (32 columns) of the row tile, then
+// for the 64 lanes L of the instruction the 8 consecutive weights
+// W[16 rt + L % 16][32 ks + 8 (L / 16) + j], j = 0..7.
+
+namespace {
+
+// Matrices end to end from 0 that cover n, rows multiples of 16, cols of 32.
+bool tiled_matrices_ok(const df11_gemv_matrix *mats, uint32_t n_mats, uint64_t n) {
+    if (!mats || n_mats < 1 || n_mats > DF11_GEMV_MAX_MATRICES) return false;
+    uint64_t off = 0;
+    for (uint32_t m = 0; m < n_mats; ++m) {
+        const df11_gemv_matrix &mm = mats[m];
+        if (mm.offset != off || mm.rows == 0 || mm.rows % 16 != 0 || mm.cols == 0 ||
+            mm.cols % 32 != 0)
+            return false;
+        off += (uint64_t)mm.rows * mm.cols;
+    }
+    return off == n;
+}
+
+}  // namespace
+
+extern "C" int df11_tile_order(const uint16_t *w, uint64_t n, const df11_gemv_matrix *mats,
+                               uint32_t n_mats, uint16_t *out, uint32_t n_threads) {
+    if (!w || !out || w == out || n == 0 || n > DF11_MAX_N) return DF11_ERR_ARG;
+    if (!tiled_matrices_ok(mats, n_mats, n)) return DF11_ERR_ARG;
+    // one task per row tile of any matrix
+    std::vector<std::pair<uint32_t, uint32_t>> tasks;  // (matrix, row tile)
+    for (uint32_t m = 0; m < n_mats; ++m)
+        for (uint32_t rt = 0; rt < mats[m].rows / 16; ++rt) tasks.emplace_back(m, rt);
+    const unsigned threads = pick_threads(n_threads, n, 1u << 20);
+    std::atomic<size_t> next{0};
+    parallel_for(threads, [&](unsigned) {
+        for (size_t t; (t = next.fetch_add(1)) < tasks.size();) {
+            const df11_gemv_matrix &mm = mats[tasks[t].first];
+            const uint64_t c = mm.cols, rt = tasks[t].second;
+            const uint16_t *src = w + mm.offset + rt * 16 * c;
+            uint16_t *dst = out + mm.offset + rt * 16 * c;
+            for (uint64_t ks = 0; ks < c / 32; ++ks)
+                for (uint32_t lane = 0; lane < 64; ++lane) {
+                    const uint16_t *row = src + (lane % 16) * c + 32 * ks + 8 * (lane / 16);
+                    std::memcpy(dst + (ks * 64 + lane) * 8, row, 16);
+                }
+        }
+    });
+    return DF11_OK;
+}
+
+extern "C" uint64_t df11_tile_segment_count(const df11_gemv_matrix *mats, uint32_t n_mats) {
+    if (!mats || n_mats < 1 || n_mats > DF11_GEMV_MAX_MATRICES) return 0;
+    uint64_t s = 0;
+    for (uint32_t m = 0; m < n_mats; ++m) s += mats[m].rows / 16;
+    return s;
+}
+
+extern "C" int df11_tile_segments(const uint32_t *block_pos, uint32_t n_blocks,
+                                  const df11_gemv_matrix *mats, uint32_t n_mats,
+                                  uint32_t *seg_blk, uint64_t seg_cap) {
+    if (!block_pos || !seg_blk || n_blocks == 0) return DF11_ERR_ARG;
+    if (block_pos[0] != 0) return DF11_ERR_FORMAT;
+    const uint64_t n = block_pos[n_blocks];
+    if (n == 0 || !tiled_matrices_ok(mats, n_mats, n)) return DF11_ERR_ARG;
+    const uint64_t segs = df11_tile_segment_count(mats, n_mats);
+    if (seg_cap < segs + 1) return DF11_ERR_BUFSIZE;
+    // the block holding weight q: the last block whose first code index is <= q
+    auto holder = [&](uint64_t q) {
+        const uint32_t *it = std::upper_bound(block_pos, block_pos + n_blocks, (uint32_t)q);
+        return (uint32_t)(it - block_pos) - 1;
+    };
+    uint64_t s = 0;
+    for (uint32_t m = 0; m < n_mats; ++m)
+        for (uint64_t rt = 0; rt < mats[m].rows / 16; ++rt)
+            seg_blk[s++] = holder(mats[m].offset + rt * 16 * (uint64_t)mats[m].cols);
+    seg_blk[segs] = holder(n - 1);
+    return DF11_OK;
+}

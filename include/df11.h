@@ -248,6 +248,65 @@ int df11_decode_gemm(const df11_device_stream *s, const df11_gemv_matrix *mats, 
                      uint64_t y_stride, void *workspace, uint64_t workspace_bytes,
                      void *hip_stream);
 
+/* ------------------------------------------------------------ tiled product
+ *
+ * The decompress-then-matmul step of DF11 inference (section "Architecture":
+ * a transformer block's weights are decompressed just before its matrix
+ * products) for 1 to 64 input vectors, on the matrix cores, without writing
+ * the BF16 weights anywhere.  The block's matrices are encoded in operand-tile
+ * order: each matrix (rows a multiple of 16, cols of 32) is cut into row tiles
+ * of 16 rows, each row tile into k-steps of 32 columns, and each k-step's 512
+ * weights are stored as 64 groups of 8, group L holding
+ * W[16 rt + L % 16][32 ks + 8 (L / 16) + 0..7] (the first operand of a
+ * 16x16x32 bf16 matrix instruction, lane by lane).  The permuted words are
+ * then encoded with df11_encode as any BF16 tensor (the histogram, and so the
+ * code book, does not depend on the order). */
+
+/* out[] = the n words of w[] (row-major matrices laid end to end as mats
+ * lists them) in operand-tile order.  Host memory, w != out.  n_threads = 0
+ * picks the number of hardware threads.  Errors: ARG (null, n out of range,
+ * matrices not end to end from 0 covering n, rows not a multiple of 16 or
+ * cols of 32). */
+int df11_tile_order(const uint16_t *w, uint64_t n, const df11_gemv_matrix *mats, uint32_t n_mats,
+                    uint16_t *out, uint32_t n_threads);
+
+/* Row tiles (segments) of a matrix list: the sum of rows / 16; 0 for a bad
+ * list. */
+uint64_t df11_tile_segment_count(const df11_gemv_matrix *mats, uint32_t n_mats);
+
+/* Segment table of a tile-order stream (host memory): seg_blk[s] = the block
+ * holding the first weight of segment s (segments in matrix order, row
+ * tiles in order), and seg_blk[S] = the block holding the last weight,
+ * where a block holds the weights [block_pos[b], block_pos[b + 1]).  The
+ * product decodes blocks seg_blk[s] .. seg_blk[s + 1] for segment s.
+ * seg_cap must be at least df11_tile_segment_count + 1.
+ * Errors: ARG, FORMAT (block_pos[0] != 0), BUFSIZE. */
+int df11_tile_segments(const uint32_t *block_pos, uint32_t n_blocks, const df11_gemv_matrix *mats,
+                       uint32_t n_mats, uint32_t *seg_blk, uint64_t seg_cap);
+
+#define DF11_TILED_MAX_BATCH 64
+
+/* Tiled fused product: for each vector b < batch (1..64) and matrix m,
+ * y[b * y_stride + y_offset_m + r] = sum_c W_m[r][c] * x[b * x_stride + x_offset_m + c]
+ * from a stream s of the block in operand-tile order, with seg_blk its
+ * segment table in device memory (4-byte aligned).  One workgroup per row
+ * tile decodes that tile's blocks and multiplies each 512-word operand tile
+ * with the matching inputs of 16 vectors at a time (v_mfma_f32_16x16x32_bf16:
+ * BF16 products exact in fp32, summed in fp32), its waves' sums added in a
+ * fixed order, so the result is the same on every run.  Matrices: 1..16, end
+ * to end from offset 0 covering all n weights, rows a multiple of 16, cols of
+ * 32, x_offset of 8.  x: BF16 device array, 16-byte aligned; y: fp32 device
+ * array, 4-byte aligned; strides in elements as for df11_decode_gemm (a
+ * multiple of 8 for x, below 2^32, at least every matrix's end; ignored for
+ * batch 1).  No workspace.  One kernel enqueued on hip_stream.  A block whose
+ * decoded count disagrees with block_pos is counted in s->status and left
+ * out of the sums.  Errors: those of df11_decode, ARG for a matrix list, batch
+ * or stride that breaks the rules. */
+int df11_decode_gemm_tiled(const df11_device_stream *s, const df11_gemv_matrix *mats,
+                           uint32_t n_mats, const uint32_t *seg_blk, const uint16_t *x,
+                           uint32_t batch, uint64_t x_stride, float *y, uint64_t y_stride,
+                           void *hip_stream);
+
 /* Workspace bytes df11_decode_gemm_noalloc can use (32 MiB): enough for
  * batches 1-8 on the 218 M-weight Llama-3.1-8B-shaped block and batches 1-2 on
  * the 856 M-weight Llama-3.3-70B-shaped block. */

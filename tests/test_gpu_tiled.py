@@ -1,0 +1,224 @@
+"""GPU parity of the tiled fused product (df11_decode_gemm_tiled) through the C ABI.
+
+y_b = W x_b for 1-64 input vectors, computed on the matrix cores straight from
+a DF11 stream whose weights are in operand-tile order.  The reference is the
+plain product of the original row-major BF16 weights with the BF16 inputs in
+float64 (numpy), which knows nothing of the tile order.
+
+Two kinds of check:
+  * exact: weights of magnitude below 2^-8 set to zero and inputs in
+    {-1, 0, 1}.  Every product is then a multiple of 2^-15 and every partial
+    sum a multiple of 2^-15 below 2^9 in magnitude (the tests assert it), so
+    it is exact in fp32 whatever the order or grouping of the additions, and
+    the result must equal the float64 product bit for bit.  A weight paired
+    with the wrong input, counted twice or left out shows up here.
+  * bounded: ordinary N(0, sigma) data.  Each result is formed by the matrix
+    instructions of each wave (32 products each, added to the running sum),
+    then 8 wave sums added in order.  Counting every one of the 32 additions
+    of an instruction as a separate fp32 rounding (2^-23 each, which also
+    covers truncation), a result whose wave took at most k instructions has
+    |y - ref| <= (32 k + 8) 2^-23 sum |w x|; k <= cols / 256 + 3 (its share of
+    the row tile's cols / 32 operand tiles, plus the tiles at the edges of
+    its blocks).
+The result must also be the same, bit for bit, on two runs, and nothing may be
+written past the results.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import huffman_decode_amd as hd
+from huffman_decode_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def torch():
+    import torch as t
+    if not t.cuda.is_available():
+        pytest.skip("no GPU")
+    return t
+
+
+def _say(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def _bf16_to_f64(torch, bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(
+        torch.bfloat16).float().numpy().astype(np.float64)
+
+
+def _run_tiled(torch, te, x_bits, batch, label, y_pad=5, status=None):
+    td = hd.tiled_to_device(te, status=status)
+    nx = x_bits.shape[1]
+    ny = sum(m.rows for m in te.mats)
+    x = torch.from_numpy(x_bits.view(np.int16)).cuda().view(torch.bfloat16)
+    ys = []
+    for fill in (1.0e30, -7.0):
+        y = torch.full((batch, ny + y_pad), fill, dtype=torch.float32, device="cuda")
+        _say(f"[gpu] df11_decode_gemm_tiled {label} n={te.enc.n} batch={batch} "
+             f"blocks={te.enc.sizes.n_blocks} segments={te.seg_blk.size - 1} fill={fill}")
+        hd.df11_decode_gemm_tiled(td, x[:, :nx], y[:, :ny])
+        torch.cuda.synchronize()
+        h = y.cpu().numpy()
+        assert np.all(h[:, ny:] == fill), "wrote past the results"
+        ys.append(h[:, :ny])
+    return ys
+
+
+def _reference(torch, w_bits, shapes, mats, x_bits):
+    """float64 W x of the original row-major weights, per vector, and sum |w x|."""
+    wf = _bf16_to_f64(torch, w_bits)
+    xf = _bf16_to_f64(torch, x_bits)
+    refs, mags, off = [], [], 0
+    for m, (r, c) in zip(mats, shapes):
+        W = wf[off: off + r * c].reshape(r, c)
+        X = xf[:, m.x_offset: m.x_offset + c]
+        refs.append(X @ W.T)
+        mags.append(np.abs(X) @ np.abs(W).T)
+        off += r * c
+    return refs, mags
+
+
+def _check(torch, w_bits, shapes, batch, label, exact, seed=5):
+    te = hd.encode_tiled(w_bits, shapes)
+    mats = te.mats
+    nx = max(m.x_offset + m.cols for m in mats)
+    rng = np.random.default_rng(seed)
+    if exact:
+        x_bits = np.array([0xBF80, 0, 0x3F80], np.uint16)[rng.integers(0, 3, (batch, nx))]
+    else:
+        x_bits = wl.to_bf16(rng.standard_normal((batch, nx)).astype(np.float32))
+    ys = _run_tiled(torch, te, x_bits, batch, label)
+    assert np.array_equal(ys[0].view(np.uint32), ys[1].view(np.uint32)), "not deterministic"
+    refs, mags = _reference(torch, w_bits, shapes, mats, x_bits)
+    for m, (r, c), ref, mag in zip(mats, shapes, refs, mags):
+        got = ys[0][:, m.y_offset: m.y_offset + r].astype(np.float64)
+        if exact:
+            assert mag.max() < 2.0 ** 9, "the exact case needs sums below 2^9"
+            bad = got != ref
+        else:
+            k = c // 256 + 3
+            bad = np.abs(got - ref) > (32 * k + 8) * 2.0 ** -23 * mag + 1e-30
+        assert not bad.any(), (label, batch, r, c, int(bad.sum()))
+
+
+def _exact_weights(n, seed, kind="normal"):
+    """BF16 words with every nonzero magnitude at least 2^-8 (smaller ones
+    set to +0), so that products with inputs in {-1, 0, 1} are multiples of
+    2^-15."""
+    w = wl.random_small(n, seed, kind).copy()
+    w[((w >> 7) & 0xFF) < 127 - 8] = 0
+    return w
+
+
+EXACT_SHAPES = {
+    "mixed": [(64, 4096), (32, 2048), (16, 4096), (48, 1024)],
+    # cols, and the power of two each |w| is held below (cols * 2^-c = 448)
+    "down": ([(32, 14336)], 5),
+    "down70b": ([(32, 28672)], 6),
+}
+
+
+@pytest.mark.parametrize("batch", [1, 2, 9, 16, 17, 33, 64])
+def test_tiled_exact_batches(torch, batch):
+    shapes = EXACT_SHAPES["mixed"]
+    w = _exact_weights(sum(r * c for r, c in shapes), 100 + batch)
+    _check(torch, w, shapes, batch, "exact_mixed", exact=True)
+
+
+@pytest.mark.parametrize("name", ["down", "down70b"])
+def test_tiled_exact_wide_rows(torch, name):
+    shapes, c = EXACT_SHAPES[name]
+    n = sum(r * cols for r, cols in shapes)
+    w = _exact_weights(n, 7)
+    # keep |w| < 2^-c so that a row's sum of |w| stays below 2^9
+    big = ((w >> 7) & 0xFF) >= 127 - c
+    w[big] = (w[big] & 0x807F) | np.uint16((127 - c - 1) << 7)
+    for batch in (1, 64):
+        _check(torch, w, shapes, batch, f"exact_{name}", exact=True)
+
+
+def test_tiled_exact_one_bit_codes(torch):
+    """One exponent only: 1-bit codes, 4096 words per block, so every block
+    decodes again in tile-sized passes and operand tiles straddle passes."""
+    shapes = [(32, 4096), (16, 8192)]
+    n = sum(r * c for r, c in shapes)
+    w = wl.random_small(n, 8, "single")
+    w = (w & 0x807F) | np.uint16((127 - 6) << 7)  # one exponent, 2^-6 .. 2^-5
+    for batch in (1, 20, 64):
+        _check(torch, w, shapes, batch, "exact_single", exact=True)
+
+
+def test_tiled_exact_flat_codes(torch):
+    """Uniform random words (8-bit codes, about 512 words per block) with
+    their exponents folded into [2^-8, 2^-5)."""
+    shapes = [(48, 4096)]
+    n = sum(r * c for r, c in shapes)
+    w = wl.random_small(n, 9, "uniform")
+    e = ((w >> 7) & 0xFF) % 3 + (127 - 8)
+    w = (w & 0x807F) | (e.astype(np.uint16) << 7)
+    for batch in (3, 64):
+        _check(torch, w, shapes, batch, "exact_flat", exact=True)
+
+
+@pytest.mark.parametrize("batch", [1, 16, 64])
+def test_tiled_llama8b_shapes(torch, batch):
+    wlx = wl.llama8b_block(seed=31, scale=1 / 16)
+    _check(torch, wlx.weights, [(m.rows, m.cols) for m in wlx.matrices], batch, "llama8b_1_16",
+           exact=False)
+
+
+def test_tiled_flux_and_70b_down(torch):
+    wlx = wl.flux_block(33, scale=1 / 32)
+    _check(torch, wlx.weights, [(m.rows, m.cols) for m in wlx.matrices], 40, "flux_1_32",
+           exact=False)
+    shapes = [(64, 28672)]
+    w = wl.random_small(64 * 28672, 34, "normal")
+    _check(torch, w, shapes, 64, "70b_down_rows", exact=False)
+
+
+def test_tiled_llama8b_block_full(torch):
+    wlx = wl.llama8b_block()
+    _check(torch, wlx.weights, [(m.rows, m.cols) for m in wlx.matrices], 64, "llama8b_block",
+           exact=False)
+
+
+def test_tiled_corrupt_blocks_stay_contained(torch):
+    """Flipped stream bits: the blocks whose counts no longer match are
+    counted in the status word and left out; nothing is written outside y,
+    and every segment whose blocks are all intact is still exact."""
+    import dataclasses
+    shapes = [(64, 4096), (32, 8192)]
+    w = _exact_weights(sum(r * c for r, c in shapes), 61)
+    te = hd.encode_tiled(w, shapes)
+    nb = int(te.enc.sizes.n_blocks)
+    rng = np.random.default_rng(62)
+    stream = te.enc.stream.copy()
+    hit = set()
+    for b in sorted(set(rng.choice(nb, 4, replace=False).tolist())):
+        bit = 4096 * b + int(rng.integers(0, 4096))
+        if bit < int(te.enc.sizes.total_bits):
+            stream[bit >> 3] ^= np.uint8(1 << (bit & 7))
+            hit |= {b, b - 1}
+    bad = hd.TiledEncoded(dataclasses.replace(te.enc, stream=stream), te.mats, te.seg_blk)
+    batch = 8
+    nx = max(m.x_offset + m.cols for m in te.mats)
+    x_bits = np.array([0xBF80, 0, 0x3F80], np.uint16)[rng.integers(0, 3, (batch, nx))]
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ys = _run_tiled(torch, bad, x_bits, batch, "corrupt", status=st)
+    assert int(st.item()) >= 1
+    refs, _ = _reference(torch, w, shapes, te.mats, x_bits)
+    seg, checked = 0, 0
+    for m, (r, c), ref in zip(te.mats, shapes, refs):
+        for rt in range(r // 16):
+            blocks = set(range(int(te.seg_blk[seg]), int(te.seg_blk[seg + 1]) + 1))
+            if not blocks & hit:
+                got = ys[0][:, m.y_offset + 16 * rt: m.y_offset + 16 * rt + 16].astype(np.float64)
+                assert np.array_equal(got, ref[:, 16 * rt: 16 * rt + 16]), (r, c, rt)
+                checked += 1
+            seg += 1
+    assert checked > 0

@@ -382,3 +382,49 @@ def test_noalloc_product_refuses_a_workspace_beyond_its_array():
                                             fake, 8192, None) == -2
     assert lib.df11_decode_gemm_noalloc(ctypes.byref(d), mats, 1, fake, 9, 1 << 20, fake, 8192,
                                         None) == -1
+
+
+def test_tile_order_follows_its_definition():
+    """df11_tile_order puts each word of a 16-row, 32-column operand tile where
+    the definition puts it: tile (rt, ks) of a matrix at 512 (rt * cols / 32 +
+    ks), group L at 8 L, word j: W[16 rt + L % 16][32 ks + 8 (L / 16) + j]."""
+    shapes = [(32, 64), (16, 96), (48, 32)]
+    n = sum(r * c for r, c in shapes)
+    w = np.arange(n, dtype=np.uint16)
+    mats, _, _ = hd.gemv_matrices(shapes)
+    t = hd.df11_tile_order(w, mats)
+    off = 0
+    for (r, c) in shapes:
+        W = w[off: off + r * c].reshape(r, c)
+        for rt in range(r // 16):
+            for ks in range(c // 32):
+                for L in range(64):
+                    at = off + ((rt * (c // 32) + ks) * 64 + L) * 8
+                    col = 32 * ks + 8 * (L // 16)
+                    assert np.array_equal(t[at: at + 8], W[16 * rt + L % 16, col: col + 8])
+        off += r * c
+    assert np.array_equal(np.sort(t), w)
+    # refused: rows not a multiple of 16, cols not a multiple of 32, not covering n
+    for bad in ([(24, 64)], [(16, 48)]):
+        m2, _, _ = hd.gemv_matrices(bad)
+        with pytest.raises(hd.Df11Error):
+            hd.df11_tile_order(np.zeros(sum(r * c for r, c in bad), np.uint16), m2)
+    with pytest.raises(hd.Df11Error):
+        hd.df11_tile_order(np.zeros(n + 8, np.uint16), mats)
+
+
+def test_tile_segments_match_a_search_of_block_pos():
+    """Each segment's entry is the block holding its first weight (the last
+    block whose first code index is at most that weight), and the final entry
+    the block of the last weight; checked on a real encoding with a linear
+    search."""
+    shapes = [(64, 4096), (32, 2048), (16, 8192)]
+    w = wl.random_small(sum(r * c for r, c in shapes), 3, "normal")
+    te = hd.encode_tiled(w, shapes)
+    bp = te.enc.block_pos.astype(np.int64)
+    nb = bp.size - 1
+    starts = [m.offset + rt * 16 * m.cols for m in te.mats for rt in range(m.rows // 16)]
+    holder = lambda q: max(b for b in range(nb) if bp[b] <= q)
+    want = [holder(q) for q in starts] + [holder(int(bp[nb]) - 1)]
+    assert te.seg_blk.tolist() == want
+    assert hd.library().df11_tile_segment_count(hd._mat_array(te.mats), len(te.mats)) == len(starts)
