@@ -175,6 +175,24 @@ def run_copy(args) -> int:
     return 0
 
 
+def launch_time_ms(launch, stream, reps=20, warmup=100) -> float:
+    """Average duration of launch(k) over `reps` back-to-back calls between one
+    pair of events on `stream`, after `warmup` untimed calls (the GPU's clocks
+    take about a hundred back-to-back launches to ramp up after an idle
+    stretch, such as a host-side encode)."""
+    import torch
+    for k in range(warmup):
+        launch(k)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for k in range(reps):
+        launch(k)
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps
+
+
 def gemm_ratios(wlx, out, decode_ms, stream, batches=(1, 2, 4, 16, 64), reps=10) -> dict:
     """Decode time of the block over the time of the block's bf16 GEMMs
     (y = x W^T for each of its matrices, on the decoded weights) at each batch."""
@@ -188,19 +206,11 @@ def gemm_ratios(wlx, out, decode_ms, stream, batches=(1, 2, 4, 16, 64), reps=10)
     for b in batches:
         xs = [torch.randn(b, w.shape[1], device=out.device, generator=g).to(torch.bfloat16)
               for w in mats]
-        for _ in range(2):
+
+        def block_gemms(_k):
             for x, w in zip(xs, mats):
                 torch.nn.functional.linear(x, w)
-        torch.cuda.synchronize()
-        s0 = torch.cuda.Event(enable_timing=True)
-        s1 = torch.cuda.Event(enable_timing=True)
-        s0.record(stream)
-        for _ in range(reps):
-            for x, w in zip(xs, mats):
-                torch.nn.functional.linear(x, w)
-        s1.record(stream)
-        torch.cuda.synchronize()
-        gms = s0.elapsed_time(s1) / reps
+        gms = launch_time_ms(block_gemms, stream, reps)
         # bytes a BF16 GEMM moves: the weights, x and y (bf16)
         moved = sum(2 * w.numel() + 2 * b * (w.shape[0] + w.shape[1]) for w in mats)
         res[f"batch{b}"] = {"gemm_ms": round(gms, 5), "decode_over_gemm": round(decode_ms / gms, 4),
@@ -336,16 +346,9 @@ def fused_gemv(wlx, copies, stream, reps=20) -> dict:
     x = x.to(torch.bfloat16)
     y = torch.empty(ny, dtype=torch.float32, device="cuda")
     ws = torch.empty(hd.df11_gemv_workspace_bytes(dev0), dtype=torch.uint8, device="cuda")
-    for k in range(3):
-        hd.df11_decode_gemv(copies[k % len(copies)], mats, x, y, ws, stream)
-    torch.cuda.synchronize()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record(stream)
-    for k in range(reps):
-        hd.df11_decode_gemv(copies[k % len(copies)], mats, x, y, ws, stream)
-    b.record(stream)
-    torch.cuda.synchronize()
-    return {"fused_ms": round(a.elapsed_time(b) / reps, 5)}
+    ms = launch_time_ms(lambda k: hd.df11_decode_gemv(copies[k % len(copies)], mats, x, y, ws,
+                                                      stream), stream, reps)
+    return {"fused_ms": round(ms, 5)}
 
 
 def fused_gemm(wlx, copies, stream, batch, reps=20) -> dict:
@@ -360,16 +363,9 @@ def fused_gemm(wlx, copies, stream, batch, reps=20) -> dict:
     x = x.cuda().to(torch.bfloat16)
     y = torch.empty(batch, ny, dtype=torch.float32, device="cuda")
     ws = torch.empty(hd.df11_gemm_workspace_bytes(copies[0], batch), dtype=torch.uint8, device="cuda")
-    for k in range(3):
-        hd.df11_decode_gemm(copies[k % len(copies)], mats, x, y, ws, stream)
-    torch.cuda.synchronize()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record(stream)
-    for k in range(reps):
-        hd.df11_decode_gemm(copies[k % len(copies)], mats, x, y, ws, stream)
-    b.record(stream)
-    torch.cuda.synchronize()
-    return {"fused_ms": round(a.elapsed_time(b) / reps, 5)}
+    ms = launch_time_ms(lambda k: hd.df11_decode_gemm(copies[k % len(copies)], mats, x, y, ws,
+                                                      stream), stream, reps)
+    return {"fused_ms": round(ms, 5)}
 
 
 def fused_tiled(wlx, stream, batches, n_copies=3, reps=20) -> dict:
@@ -390,16 +386,8 @@ def fused_tiled(wlx, stream, batches, n_copies=3, reps=20) -> dict:
         x = torch.from_numpy(np.random.default_rng(9).standard_normal((batch, nx)).astype(np.float32))
         x = x.cuda().to(torch.bfloat16)
         y = torch.empty(batch, ny, dtype=torch.float32, device="cuda")
-        for k in range(3):
-            hd.df11_decode_gemm_tiled(copies[k % n_copies], x, y, stream)
-        torch.cuda.synchronize()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        for k in range(reps):
-            hd.df11_decode_gemm_tiled(copies[k % n_copies], x, y, stream)
-        b.record(stream)
-        torch.cuda.synchronize()
-        ms = a.elapsed_time(b) / reps
+        ms = launch_time_ms(lambda k: hd.df11_decode_gemm_tiled(copies[k % n_copies], x, y, stream),
+                            stream, reps)
         res[f"batch{batch}"] = {"fused_ms": round(ms, 5),
                                 "fused_gbs": round((rd + 2 * batch * nx + 4 * batch * ny)
                                                    / (ms * 1e-3) / 1e9, 1)}

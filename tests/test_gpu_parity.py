@@ -225,7 +225,8 @@ def test_fused_gemv_with_corrupt_blocks(torch):
             W = wf[rs:re]
             xv = xv_all[m.x_offset: m.x_offset + c].astype(np.float64)
             ref = W @ xv
-            bound = np.abs(W) @ np.abs(xv) * 2.0 ** -18 + 1e-30
+            k = 30 + block_of(re - 1) - block_of(rs) + 1
+            bound = np.abs(W) @ np.abs(xv) * k * 2.0 ** -24 + 1e-30
             assert abs(got[m.y_offset + row] - ref) <= bound, (m.rows, row)
             checked += 1
         off += r * c
@@ -380,12 +381,26 @@ def test_capped_decode_grid(torch, small_stack, groups):
 
 # ---------------------------------------------------------------------------
 # Fused decode + GEMV.  Reference: the plain product of the original BF16
-# weights with the BF16 x, both as float64, by numpy.  BF16 x BF16 products are
-# exact in fp32; the kernel forms each row's sum in fp32 with at most 8 (per
-# group) + 16 (groups per lane) + 6 (wave tree) + 16 (blocks per row, cols <=
-# 16384 over >= 1000 weights per block) = 46 rounded additions, so
-# |y - ref| <= 46 * 2^-24 * sum|w x| bounds the error; the test uses
-# 2^-18 * sum|w x| (64 * 2^-24).
+# weights with the BF16 x, both as float64, by numpy.  BF16 x BF16 products
+# are exact in fp32.  A row's sum is formed with: per 8-word group, four packed
+# dot instructions (each counted as 2 roundings, and at twice the unit
+# roundoff in case it truncates: 16 units); the group added to the lane's sum
+# (at most 8 groups per lane per block: 8); the wave's 64-lane sum (6); and
+# one addition per block that holds words of the row.  So |y - ref| <=
+# (30 + B_row) 2^-24 sum |w x|, with B_row the blocks the row touches, taken
+# from block_pos.  (For rows of 28672 words in 512-word blocks, B_row is 57.)
+
+def _row_bounds(enc, mats, shapes):
+    """Per matrix, the rounding count 30 + B_row of each row."""
+    bp = enc.block_pos.astype(np.int64)
+    out = []
+    for m, (r, c) in zip(mats, shapes):
+        rs = m.offset + c * np.arange(r, dtype=np.int64)
+        first = np.searchsorted(bp, rs, side="right") - 1
+        last = np.searchsorted(bp, rs + c - 1, side="right") - 1
+        out.append(30 + (last - first + 1))
+    return out
+
 
 def _gemv_check(torch, w, shapes, label, seed=7):
     enc = hd.encode(w)
@@ -406,11 +421,11 @@ def _gemv_check(torch, w, shapes, label, seed=7):
     assert np.array_equal(ys[0].view(np.uint32), ys[1].view(np.uint32)), "not deterministic"
     wf = torch.from_numpy(w.view(np.int16)).view(torch.bfloat16).float().numpy().astype(np.float64)
     off = 0
-    for m, (r, c) in zip(mats, shapes):
+    for m, (r, c), k in zip(mats, shapes, _row_bounds(enc, mats, shapes)):
         W = wf[off: off + r * c].reshape(r, c)
         xv = x_host[m.x_offset: m.x_offset + c].astype(np.float64)
         ref = W @ xv
-        bound = np.abs(W) @ np.abs(xv) * 2.0 ** -18 + 1e-30
+        bound = np.abs(W) @ np.abs(xv) * k * 2.0 ** -24 + 1e-30
         got = ys[0][m.y_offset: m.y_offset + r].astype(np.float64)
         bad = np.abs(got - ref) > bound
         assert not bad.any(), (label, m.rows, m.cols, int(bad.sum()))
@@ -440,6 +455,26 @@ def test_fused_gemv_llama8b_block(torch):
     _gemv_check(torch, wlx.weights, [(m.rows, m.cols) for m in wlx.matrices], "llama8b_block")
 
 
+def _flat_exponents(n, seed):
+    """Words whose exponents are spread evenly over 127 values (7-bit codes,
+    about 580 words per block), all finite: sign and mantissa random."""
+    rng = np.random.default_rng(seed)
+    e = rng.integers(64, 191, n).astype(np.uint16)
+    return (rng.integers(0, 1 << 16, n).astype(np.uint16) & 0x807F) | (e << 7)
+
+
+@pytest.mark.parametrize("kind", ["normal", "flat"])
+def test_fused_gemv_70b_down_rows(torch, kind):
+    """Rows of the 70B-shaped down matrix (28672 columns): with flat exponents
+    a row spans about 50 blocks, beyond what a fixed bound of 46 roundings
+    would cover; the per-row bound follows the stream."""
+    shapes = [(8, 28672)]
+    n = 8 * 28672
+    w = wl.random_small(n, 51, "normal") if kind == "normal" else _flat_exponents(n, 52)
+    _gemv_check(torch, w, shapes, f"70b_down_{kind}")
+    _gemm_check(torch, w, shapes, f"70b_down_{kind}", 3)
+
+
 # Fused decode + product with several input vectors: each vector's result is
 # checked like the batch-1 one, and must equal, bit for bit, what the batch-1
 # call gives for that vector alone (the same sums in the same order).
@@ -465,13 +500,14 @@ def _gemm_check(torch, w, shapes, label, batch, seed=17, x_pad=24, y_pad=5):
     assert np.all(ys[0][:, ny:] == 1.0e30) and np.all(ys[1][:, ny:] == -7.0), "wrote past the results"
     wf = torch.from_numpy(w.view(np.int16)).view(torch.bfloat16).float().numpy().astype(np.float64)
     ws1 = torch.empty(hd.df11_gemv_workspace_bytes(dev), dtype=torch.uint8, device="cuda")
+    ks = _row_bounds(enc, mats, shapes)
     for b in range(batch):
         off = 0
-        for m, (r, c) in zip(mats, shapes):
+        for m, (r, c), k in zip(mats, shapes, ks):
             W = wf[off: off + r * c].reshape(r, c)
             xv = x_host[b, m.x_offset: m.x_offset + c].astype(np.float64)
             ref = W @ xv
-            bound = np.abs(W) @ np.abs(xv) * 2.0 ** -18 + 1e-30
+            bound = np.abs(W) @ np.abs(xv) * k * 2.0 ** -24 + 1e-30
             got = ys[0][b, m.y_offset: m.y_offset + r].astype(np.float64)
             bad = np.abs(got - ref) > bound
             assert not bad.any(), (label, b, m.rows, m.cols, int(bad.sum()))

@@ -48,16 +48,19 @@ def _case(torch, wlx, batch, seed):
     got, ref = y.cpu().numpy(), y_ref.cpu().numpy()
     assert np.all(got[:, ny:] == -3.0), "wrote past the results"
     assert np.array_equal(got[:, :ny].view(np.uint32), ref[:, :ny].view(np.uint32))
-    # and within the bound against fp64 (2^-18 sum |w x|: at most 46 rounded
-    # additions per sum at these shapes)
+    # and within the fused product's bound against fp64: (30 + B_row) 2^-24
+    # sum |w x|, B_row the blocks the row touches (see test_gpu_parity.py)
     wf = torch.from_numpy(wlx.weights.view(np.int16)).view(torch.bfloat16).float().numpy()
     xf = torch.from_numpy(x_bits.view(np.int16)).view(torch.bfloat16).float().numpy()
+    bp = enc.block_pos.astype(np.int64)
     off = 0
     for m, (r, c) in zip(mats, shapes):
         W = wf[off: off + r * c].reshape(r, c).astype(np.float64)
+        rs = off + c * np.arange(r, dtype=np.int64)
+        k = 31 + np.searchsorted(bp, rs + c - 1, side="right") - np.searchsorted(bp, rs, side="right")
         for b in range(batch):
             xv = xf[b, m.x_offset: m.x_offset + c].astype(np.float64)
-            bound = np.abs(W) @ np.abs(xv) * 2.0 ** -18 + 1e-30
+            bound = np.abs(W) @ np.abs(xv) * k * 2.0 ** -24 + 1e-30
             assert np.all(np.abs(got[b, m.y_offset: m.y_offset + r] - W @ xv) <= bound)
         off += r * c
 
