@@ -386,8 +386,10 @@ def fused_tiled(wlx, stream, batches, n_copies=3, reps=20) -> dict:
         x = torch.from_numpy(np.random.default_rng(9).standard_normal((batch, nx)).astype(np.float32))
         x = x.cuda().to(torch.bfloat16)
         y = torch.empty(batch, ny, dtype=torch.float32, device="cuda")
-        ms = launch_time_ms(lambda k: hd.df11_decode_gemm_tiled(copies[k % n_copies], x, y, stream),
-                            stream, reps)
+        need = hd.df11_tiled_workspace_bytes(te.mats, batch)
+        ws = torch.empty(need, dtype=torch.uint8, device="cuda") if need else None
+        ms = launch_time_ms(lambda k: hd.df11_decode_gemm_tiled(copies[k % n_copies], x, y, ws,
+                                                                stream), stream, reps)
         res[f"batch{batch}"] = {"fused_ms": round(ms, 5),
                                 "fused_gbs": round((rd + 2 * batch * nx + 4 * batch * ny)
                                                    / (ms * 1e-3) / 1e9, 1)}

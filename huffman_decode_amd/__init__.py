@@ -118,8 +118,10 @@ def _load():
         lib.df11_tile_segments.restype = ctypes.c_int
         lib.df11_decode_gemm_tiled.argtypes = [ctypes.POINTER(DeviceStream),
                                                ctypes.POINTER(GemvMatrix), _U32, _P, _P, _U32,
-                                               _U64, _P, _U64, _P]
+                                               _U64, _P, _U64, _P, _U64, _P]
         lib.df11_decode_gemm_tiled.restype = ctypes.c_int
+        lib.df11_tiled_workspace_bytes.argtypes = [ctypes.POINTER(GemvMatrix), _U32, _U32]
+        lib.df11_tiled_workspace_bytes.restype = _U64
         lib.df11_stream_ceiling.argtypes = [_P, _P, _U64, _P, _U64, _U32, _P]
         lib.df11_stream_ceiling.restype = ctypes.c_int
         _lib = lib
@@ -491,18 +493,31 @@ def tiled_to_device(te: TiledEncoded, device="cuda", status=None) -> TiledDevice
     return TiledDevice(dev, te.mats, seg)
 
 
-def df11_decode_gemm_tiled(td: TiledDevice, x, y, stream=None) -> None:
+def df11_tiled_workspace_bytes(mats: list[GemvMatrix], batch: int) -> int:
+    return int(_load().df11_tiled_workspace_bytes(_mat_array(mats), len(mats), batch))
+
+
+def df11_decode_gemm_tiled(td: TiledDevice, x, y, workspace=None, stream=None) -> None:
     """Enqueue y[b] = W x[b] for every matrix and every row b of x (batch
     1..64) from a tile-order stream, on the matrix cores (x [batch, nx]
-    bfloat16, y [batch, ny] float32, unit column stride; no workspace)."""
+    bfloat16, y [batch, ny] float32, unit column stride; workspace a CUDA
+    tensor of at least df11_tiled_workspace_bytes bytes, None when that is 0)."""
     import torch
     _check_gemm_xy(td.dev, td.mats, x, y)
     _same_device(td.dev, seg_blk=td.seg_blk)
+    need = df11_tiled_workspace_bytes(td.mats, x.shape[0])
+    ws_ptr, ws_bytes = 0, 0
+    if workspace is not None:
+        _same_device(td.dev, workspace=workspace)
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    if ws_bytes < need:
+        raise ValueError(f"the tiled product needs a workspace of {need} bytes")
     if stream is None:
         stream = torch.cuda.current_stream(y.device)
     _check("df11_decode_gemm_tiled", _load().df11_decode_gemm_tiled(
         ctypes.byref(td.dev.desc), _mat_array(td.mats), len(td.mats), td.seg_blk.data_ptr(),
-        x.data_ptr(), x.shape[0], x.stride(0), y.data_ptr(), y.stride(0), stream.cuda_stream))
+        x.data_ptr(), x.shape[0], x.stride(0), y.data_ptr(), y.stride(0), ws_ptr, ws_bytes,
+        stream.cuda_stream))
 
 
 # ------------------------------------------------------------ measurement aid

@@ -1169,6 +1169,11 @@ constexpr int kTiledMaxBatch = 64;
 
 struct TiledArgs {
     const uint16_t *x;        // matrix m's inputs at x + xoff; vector b at + b * x_stride
+    // or, when xt is set, the inputs rewritten k-step-major by
+    // df11_tile_inputs_kernel: element (k-step ks, vector b, column c) of the
+    // range at column offset xoff (xoff then counts columns of xt) at
+    // xt[16 NT (xoff + 32 ks) + 32 b + c]
+    const uint16_t *xt;
     float *y;                 // matrix m's results at y + yoff; vector b at + b * y_stride
     const uint32_t *seg_blk;  // per segment (matrix order) its first block; then the last block
     uint64_t x_stride, y_stride;
@@ -1215,8 +1220,9 @@ __device__ __forceinline__ uint2 tile_sm(const uint8_t *signmant, uint32_t tt, u
 // batch, inputs xl + 16 nt x_stride + 32 ks + 0..7 for k-step ks (xl already
 // holds the lane's vector, the matrix's x offset and the lane's 8 columns).
 struct XSrc {
-    const g_cu16 *xl;
-    uint64_t group_stride;  // 16 x_stride: from one group of 16 vectors to the next
+    const g_cu16 *xl;       // the lane's 8 inputs of group 0, k-step 0
+    uint64_t group_stride;  // from one group of 16 vectors to the next
+    uint64_t ks_stride;     // from one k-step to the next
     uint32_t live;          // vectors of the lane's column below the batch: bit nt
 };
 
@@ -1226,7 +1232,7 @@ __device__ __forceinline__ void tile_x(u32x4 (&bv)[NT], const XSrc &xs, uint32_t
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
         bv[nt] = (xs.live >> nt) & 1u
-                     ? *(const g_cu32x4 *)(xs.xl + nt * xs.group_stride + 32 * ks)
+                     ? *(const g_cu32x4 *)(xs.xl + nt * xs.group_stride + ks * xs.ks_stride)
                      : u32x4{0, 0, 0, 0};
 }
 
@@ -1274,6 +1280,41 @@ __device__ __forceinline__ void mfma_window(uint32_t w_lo, uint32_t w_hi, uint32
         const uint2 sm = tile_sm(signmant, tt, w_lo, w_hi, lane);
         tile_mfma<NT>(acc, tile_a(tile, t_base, sm, tt, w_lo, w_hi, lane), bv);
     }
+}
+
+// Input ranges for df11_tile_inputs_kernel: range r is x[b * x_stride +
+// xoff[r] + c], c < cols[r], rewritten from column offset txoff[r] of xt.
+struct TileInputs {
+    const uint16_t *x;
+    uint16_t *xt;
+    uint64_t x_stride;
+    uint32_t batch, rows;  // vectors in use; vectors per k-step slab of xt (16 NT)
+    uint32_t n_ranges;
+    uint32_t first[kGemvMaxMats + 1];  // first 16-byte chunk of each range; then the total
+    uint32_t xoff[kGemvMaxMats];
+    uint32_t cols[kGemvMaxMats];
+    uint32_t txoff[kGemvMaxMats];
+};
+
+// x (row-major, one row per vector) -> xt (per range, per 32-column k-step,
+// a slab of `rows` vectors x 32 columns), one 16-byte chunk per thread:
+// consecutive threads read consecutive chunks of one row of x.  Slab rows of
+// vectors at or past the batch are not written (the product never reads them).
+__global__ __launch_bounds__(256) void df11_tile_inputs_kernel(TileInputs t) {
+    const uint32_t id = blockIdx.x * 256 + threadIdx.x;
+    if (id >= t.first[t.n_ranges]) return;
+    uint32_t r = 0;
+#pragma unroll
+    for (int i = 1; i < kGemvMaxMats; ++i) r += ((uint32_t)i < t.n_ranges && id >= t.first[i]) ? 1u : 0u;
+    uint32_t first_r = 0, xoff_r = 0, cols_r = 0, txoff_r = 0;
+#pragma unroll
+    for (int i = 0; i < kGemvMaxMats; ++i)
+        if ((uint32_t)i == r) first_r = t.first[i], xoff_r = t.xoff[i], cols_r = t.cols[i], txoff_r = t.txoff[i];
+    const uint32_t k = id - first_r, per_row = cols_r / 8;
+    const uint32_t b = k / per_row, c8 = k % per_row;  // vector, chunk of 8 columns
+    const u32x4 v = *(const g_cu32x4 *)((const g_cu16 *)t.x + (uint64_t)b * t.x_stride + xoff_r + 8 * c8);
+    const uint64_t at = (uint64_t)t.rows * (txoff_r + 32 * (c8 / 4)) + 32 * b + 8 * (c8 % 4);
+    *(__attribute__((address_space(1))) u32x4 *)((__attribute__((address_space(1))) uint16_t *)t.xt + at) = v;
 }
 
 // Occupancy: up to 32 vectors the decode's 80-VGPR budget (3 workgroups per
@@ -1326,8 +1367,15 @@ void df11_tiled_kernel(DecodeArgs a, TiledArgs t) {
     // the lane's B operand: vector 16 nt + lane % 16, columns 8 (lane / 16)
     // + 0..7 of each 32-column slab
     XSrc xs;
-    xs.xl = (const g_cu16 *)t.x + (uint64_t)(lane % 16) * t.x_stride + xoff_e + 8 * (lane / 16);
-    xs.group_stride = 16 * t.x_stride;
+    if (t.xt) {  // inputs rewritten k-step-major: [k-step][16 NT vectors][32 columns]
+        xs.xl = (const g_cu16 *)t.xt + (uint64_t)xoff_e * (16 * NT) + (lane % 16) * 32 + 8 * (lane / 16);
+        xs.group_stride = 16 * 32;
+        xs.ks_stride = 32 * 16 * NT;
+    } else {  // row-major x
+        xs.xl = (const g_cu16 *)t.x + (uint64_t)(lane % 16) * t.x_stride + xoff_e + 8 * (lane / 16);
+        xs.group_stride = 16 * t.x_stride;
+        xs.ks_stride = 32;
+    }
     xs.live = 0;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) xs.live |= (16 * nt + lane % 16 < t.batch ? 1u : 0u) << nt;
@@ -1715,10 +1763,46 @@ extern "C" int df11_decode_gemm_noalloc(const df11_device_stream *s, const df11_
 
 // ------------------------------------------------------------ tiled product launch
 
+// Batches from this size on read their inputs rewritten k-step-major: a wave's
+// 16 B loads of one k-step then cover 1 KB in one piece instead of 64 bytes
+// of each of 16 rows, which the memory pipeline serves far faster (batch 64:
+// 0.34 -> 0.23 ms on the 8B-shaped block).  Smaller batches read x directly.
+constexpr uint32_t kTiledRewriteBatch = 8;
+
+static uint32_t tiled_groups(uint32_t batch) { return batch <= 16 ? 1u : batch <= 32 ? 2u : 4u; }
+
+// The distinct input ranges (x_offset, cols) of a matrix list, in order of
+// first use; range_of[m] is matrix m's.
+static uint32_t input_ranges(const df11_gemv_matrix *mats, uint32_t n_mats, uint32_t *xoff,
+                             uint32_t *cols, uint32_t *range_of) {
+    uint32_t n = 0;
+    for (uint32_t m = 0; m < n_mats; ++m) {
+        uint32_t r = 0;
+        while (r < n && !(xoff[r] == mats[m].x_offset && cols[r] == mats[m].cols)) ++r;
+        if (r == n) xoff[n] = mats[m].x_offset, cols[n] = mats[m].cols, ++n;
+        range_of[m] = r;
+    }
+    return n;
+}
+
+extern "C" uint64_t df11_tiled_workspace_bytes(const df11_gemv_matrix *mats, uint32_t n_mats,
+                                               uint32_t batch) {
+    if (!mats || n_mats < 1 || n_mats > (uint32_t)kGemvMaxMats || batch < 1 ||
+        batch > (uint32_t)kTiledMaxBatch)
+        return 0;
+    if (batch < kTiledRewriteBatch) return 0;
+    uint32_t xoff[kGemvMaxMats], cols[kGemvMaxMats], range_of[kGemvMaxMats];
+    const uint32_t nr = input_ranges(mats, n_mats, xoff, cols, range_of);
+    uint64_t total = 0;
+    for (uint32_t r = 0; r < nr; ++r) total += cols[r];
+    return 2ull * 16 * tiled_groups(batch) * total;
+}
+
 extern "C" int df11_decode_gemm_tiled(const df11_device_stream *s, const df11_gemv_matrix *mats,
                                       uint32_t n_mats, const uint32_t *seg_blk, const uint16_t *x,
                                       uint32_t batch, uint64_t x_stride, float *y,
-                                      uint64_t y_stride, void *hip_stream) {
+                                      uint64_t y_stride, void *workspace, uint64_t workspace_bytes,
+                                      void *hip_stream) {
     if (!mats || !seg_blk || !x || !y) return DF11_ERR_ARG;
     DecodeArgs a;
     int st = prepare(s, nullptr, &a);
@@ -1745,6 +1829,40 @@ extern "C" int df11_decode_gemm_tiled(const df11_device_stream *s, const df11_ge
     }
     if (off != s->n) return DF11_ERR_ARG;
     if (batch > 1 && (x_stride < x_end || y_stride < y_end)) return DF11_ERR_ARG;
+    const bool rewrite = batch >= kTiledRewriteBatch;
+    const uint64_t need = df11_tiled_workspace_bytes(mats, n_mats, batch);
+    if (rewrite && (!workspace || !aligned(workspace, 16))) return DF11_ERR_ARG;
+    if (workspace_bytes < need) return DF11_ERR_BUFSIZE;
+    const uint32_t groups = tiled_groups(batch);
+    const hipStream_t hs = static_cast<hipStream_t>(hip_stream);
+
+    // the inputs, rewritten k-step-major into the workspace
+    uint32_t rxoff[kGemvMaxMats], rcols[kGemvMaxMats], range_of[kGemvMaxMats], rtx[kGemvMaxMats];
+    const uint32_t nr = input_ranges(mats, n_mats, rxoff, rcols, range_of);
+    if (rewrite) {
+        TileInputs ti;
+        std::memset(&ti, 0, sizeof(ti));
+        ti.x = x;
+        ti.xt = static_cast<uint16_t *>(workspace);
+        ti.x_stride = batch > 1 ? x_stride : 0;
+        ti.batch = batch;
+        ti.rows = 16 * groups;
+        ti.n_ranges = nr;
+        uint64_t chunks = 0, tx = 0;
+        for (uint32_t r = 0; r < nr; ++r) {
+            ti.first[r] = (uint32_t)chunks;
+            ti.xoff[r] = rxoff[r];
+            ti.cols[r] = rcols[r];
+            ti.txoff[r] = rtx[r] = (uint32_t)tx;
+            chunks += (uint64_t)batch * (rcols[r] / 8);
+            tx += rcols[r];
+        }
+        if (chunks >= (1ull << 31)) return DF11_ERR_ARG;
+        ti.first[nr] = (uint32_t)chunks;
+        hipLaunchKernelGGL(df11_tile_inputs_kernel, dim3((uint32_t)((chunks + 255) / 256)), dim3(256),
+                           0, hs, ti);
+    }
+
     // launch order: matrices by decreasing cols (their segments take longest)
     uint32_t order[kGemvMaxMats];
     for (uint32_t m = 0; m < n_mats; ++m) order[m] = m;
@@ -1753,6 +1871,7 @@ extern "C" int df11_decode_gemm_tiled(const df11_device_stream *s, const df11_ge
     TiledArgs t;
     std::memset(&t, 0, sizeof(t));
     t.x = x;
+    t.xt = rewrite ? static_cast<const uint16_t *>(workspace) : nullptr;
     t.y = y;
     t.seg_blk = seg_blk;
     t.x_stride = batch > 1 ? x_stride : 0;
@@ -1766,16 +1885,15 @@ extern "C" int df11_decode_gemm_tiled(const df11_device_stream *s, const df11_ge
         t.tile0[e] = (uint32_t)(mm.offset / 512);
         t.ksteps[e] = mm.cols / 32;
         t.seg0[e] = seg0[order[e]];
-        t.xoff[e] = mm.x_offset;
+        t.xoff[e] = rewrite ? rtx[range_of[order[e]]] : mm.x_offset;
         t.yoff[e] = mm.y_offset;
         run += mm.rows / 16;
     }
     t.first[n_mats] = run;
-    const hipStream_t hs = static_cast<hipStream_t>(hip_stream);
     const dim3 grid(run), block(kGroupThreads);
     const size_t lds = lds_bytes(s->n_tables);
-    if (batch <= 16) hipLaunchKernelGGL(df11_tiled_kernel<1>, grid, block, lds, hs, a, t);
-    else if (batch <= 32) hipLaunchKernelGGL(df11_tiled_kernel<2>, grid, block, lds, hs, a, t);
+    if (groups == 1) hipLaunchKernelGGL(df11_tiled_kernel<1>, grid, block, lds, hs, a, t);
+    else if (groups == 2) hipLaunchKernelGGL(df11_tiled_kernel<2>, grid, block, lds, hs, a, t);
     else hipLaunchKernelGGL(df11_tiled_kernel<4>, grid, block, lds, hs, a, t);
     return hipGetLastError() == hipSuccess ? DF11_OK : DF11_ERR_HIP;
 }

@@ -286,6 +286,13 @@ int df11_tile_segments(const uint32_t *block_pos, uint32_t n_blocks, const df11_
 
 #define DF11_TILED_MAX_BATCH 64
 
+/* Bytes of device workspace df11_decode_gemm_tiled needs for this matrix list
+ * and batch: 0 below 8 vectors; from 8 on, room for the inputs rewritten
+ * k-step-major (2 bytes x 16 vectors per group of 16 in the batch x the
+ * columns of the distinct input ranges (x_offset, cols)).  0 also for a bad
+ * list or batch. */
+uint64_t df11_tiled_workspace_bytes(const df11_gemv_matrix *mats, uint32_t n_mats, uint32_t batch);
+
 /* Tiled fused product: for each vector b < batch (1..64) and matrix m,
  * y[b * y_stride + y_offset_m + r] = sum_c W_m[r][c] * x[b * x_stride + x_offset_m + c]
  * from a stream s of the block in operand-tile order, with seg_blk its
@@ -298,14 +305,19 @@ int df11_tile_segments(const uint32_t *block_pos, uint32_t n_blocks, const df11_
  * 32, x_offset of 8.  x: BF16 device array, 16-byte aligned; y: fp32 device
  * array, 4-byte aligned; strides in elements as for df11_decode_gemm (a
  * multiple of 8 for x, below 2^32, at least every matrix's end; ignored for
- * batch 1).  No workspace.  One kernel enqueued on hip_stream.  A block whose
- * decoded count disagrees with block_pos is counted in s->status and left
- * out of the sums.  Errors: those of df11_decode, ARG for a matrix list, batch
- * or stride that breaks the rules. */
+ * batch 1).  workspace: caller-owned device memory of at least
+ * df11_tiled_workspace_bytes (16-byte aligned; may be null when that is 0),
+ * overwritten: from 8 vectors on, a first kernel copies the inputs there
+ * k-step-major ([k-step][vector][32 columns]), so that each wave's loads of
+ * one k-step read one contiguous kilobyte.  One or two kernels enqueued on
+ * hip_stream.  A block whose decoded count disagrees with block_pos is
+ * counted in s->status and left out of the sums.  Errors: those of
+ * df11_decode, ARG for a matrix list, batch, stride or workspace pointer that
+ * breaks the rules, BUFSIZE for a short workspace. */
 int df11_decode_gemm_tiled(const df11_device_stream *s, const df11_gemv_matrix *mats,
                            uint32_t n_mats, const uint32_t *seg_blk, const uint16_t *x,
                            uint32_t batch, uint64_t x_stride, float *y, uint64_t y_stride,
-                           void *hip_stream);
+                           void *workspace, uint64_t workspace_bytes, void *hip_stream);
 
 /* Workspace bytes df11_decode_gemm_noalloc can use (32 MiB): enough for
  * batches 1-8 on the 218 M-weight Llama-3.1-8B-shaped block and batches 1-2 on

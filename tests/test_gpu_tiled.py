@@ -56,12 +56,14 @@ def _run_tiled(torch, te, x_bits, batch, label, y_pad=5, status=None):
     nx = x_bits.shape[1]
     ny = sum(m.rows for m in te.mats)
     x = torch.from_numpy(x_bits.view(np.int16)).cuda().view(torch.bfloat16)
+    need = hd.df11_tiled_workspace_bytes(te.mats, batch)
+    ws = torch.full((need,), 0x7F, dtype=torch.uint8, device="cuda") if need else None
     ys = []
     for fill in (1.0e30, -7.0):
         y = torch.full((batch, ny + y_pad), fill, dtype=torch.float32, device="cuda")
         _say(f"[gpu] df11_decode_gemm_tiled {label} n={te.enc.n} batch={batch} "
              f"blocks={te.enc.sizes.n_blocks} segments={te.seg_blk.size - 1} fill={fill}")
-        hd.df11_decode_gemm_tiled(td, x[:, :nx], y[:, :ny])
+        hd.df11_decode_gemm_tiled(td, x[:, :nx], y[:, :ny], ws)
         torch.cuda.synchronize()
         h = y.cpu().numpy()
         assert np.all(h[:, ny:] == fill), "wrote past the results"
@@ -83,8 +85,11 @@ def _reference(torch, w_bits, shapes, mats, x_bits):
     return refs, mags
 
 
-def _check(torch, w_bits, shapes, batch, label, exact, seed=5):
+def _check(torch, w_bits, shapes, batch, label, exact, seed=5, shared_x=False):
     te = hd.encode_tiled(w_bits, shapes)
+    if shared_x:  # every matrix reads the same inputs (as q, k and v do)
+        for m in te.mats:
+            m.x_offset = 0
     mats = te.mats
     nx = max(m.x_offset + m.cols for m in mats)
     rng = np.random.default_rng(seed)
@@ -128,6 +133,15 @@ def test_tiled_exact_batches(torch, batch):
     shapes = EXACT_SHAPES["mixed"]
     w = _exact_weights(sum(r * c for r, c in shapes), 100 + batch)
     _check(torch, w, shapes, batch, "exact_mixed", exact=True)
+
+
+@pytest.mark.parametrize("batch", [8, 64])
+def test_tiled_exact_shared_inputs(torch, batch):
+    """Matrices that read the same input range: the inputs are rewritten once
+    for all of them."""
+    shapes = [(64, 4096), (32, 4096), (16, 4096)]
+    w = _exact_weights(sum(r * c for r, c in shapes), 40 + batch)
+    _check(torch, w, shapes, batch, "exact_shared_x", exact=True, shared_x=True)
 
 
 @pytest.mark.parametrize("name", ["down", "down70b"])

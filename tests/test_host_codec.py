@@ -428,3 +428,41 @@ def test_tile_segments_match_a_search_of_block_pos():
     want = [holder(q) for q in starts] + [holder(int(bp[nb]) - 1)]
     assert te.seg_blk.tolist() == want
     assert hd.library().df11_tile_segment_count(hd._mat_array(te.mats), len(te.mats)) == len(starts)
+
+
+def test_tiled_workspace_size_and_refusal():
+    """The tiled product's workspace holds the inputs rewritten k-step-major
+    from 8 vectors on: 2 bytes x 16 per group of 16 vectors x the columns of
+    the distinct input ranges; a shorter workspace is refused before any
+    device call."""
+    lib = hd.library()
+    shapes = [(64, 4096), (32, 2048)]
+    mats, _, _ = hd.gemv_matrices(shapes)
+    assert hd.df11_tiled_workspace_bytes(mats, 1) == 0
+    assert hd.df11_tiled_workspace_bytes(mats, 7) == 0
+    assert hd.df11_tiled_workspace_bytes(mats, 8) == 2 * 16 * (4096 + 2048)
+    assert hd.df11_tiled_workspace_bytes(mats, 33) == 2 * 64 * (4096 + 2048)
+    assert hd.df11_tiled_workspace_bytes(mats, 65) == 0
+    shared = [hd.GemvMatrix(0, 64, 4096, 0, 0), hd.GemvMatrix(64 * 4096, 32, 4096, 0, 64)]
+    assert hd.df11_tiled_workspace_bytes(shared, 20) == 2 * 32 * 4096
+    n = sum(r * c for r, c in shapes)
+    te = hd.encode_tiled(wl.random_small(n, 4, "normal"), shapes)
+    sz = te.enc.sizes
+    d = hd.DeviceStream()
+    fake = 1 << 20
+    d.stream = d.gaps = d.block_pos = d.signmant = d.luts = fake
+    d.stream_bytes, d.gaps_bytes = sz.stream_bytes, sz.gaps_bytes
+    d.block_pos_count, d.signmant_bytes, d.lut_bytes = sz.block_pos_count, sz.signmant_bytes, \
+        sz.lut_bytes
+    d.n, d.total_bits, d.last_start = sz.n, sz.total_bits, sz.last_start
+    d.n_blocks, d.n_tables, d.max_len = sz.n_blocks, te.enc.codebook.n_tables, \
+        te.enc.codebook.max_len
+    arr = hd._mat_array(mats)
+    need = hd.df11_tiled_workspace_bytes(mats, 16)
+    assert lib.df11_decode_gemm_tiled(ctypes.byref(d), arr, 2, fake, fake, 16, 6144, fake, 96,
+                                      fake, need - 16, None) == -2
+    assert lib.df11_decode_gemm_tiled(ctypes.byref(d), arr, 2, fake, fake, 65, 6144, fake, 96,
+                                      fake, need, None) == -1
+    bad = hd._mat_array(hd.gemv_matrices([(24, 4096), (40, 2048)])[0])
+    assert lib.df11_decode_gemm_tiled(ctypes.byref(d), bad, 2, fake, fake, 2, 6144, fake, 96,
+                                      fake, need, None) == -1
