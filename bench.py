@@ -237,10 +237,12 @@ def run_stack(args) -> int:
         wlx = wl.llama8b_stack_block(layer)
         t0 = time.perf_counter()
         enc = hd.encode(wlx.weights)
-        t_enc += time.perf_counter() - t0
         d = hd.to_device(enc, dev)
         shapes = [(m.rows, m.cols) for m in wlx.matrices]
-        blocks.append(StackBlock(d, shapes))
+        te = hd.encode_tiled(wlx.weights, shapes)
+        t_enc += time.perf_counter() - t0
+        blocks.append(StackBlock(d, shapes, hd.tiled_to_device(te, dev)))
+        del te
         # the decoded copy doubles as the resident BF16 weights of the GEMM-only pass
         buf = torch.empty(enc.n, dtype=torch.bfloat16, device=dev)
         hd.df11_decode(d, buf)
@@ -264,7 +266,7 @@ def run_stack(args) -> int:
         return e0.elapsed_time(e1) / reps
 
     res = {}
-    for batch in (1, 4, 64):
+    for batch in (1, 4, 16, 64):
         acts, outs = runner.activations(batch)
         t_dec = timed(runner.run_decodes_only, args.steps)
         t_gemm = timed(lambda: runner.run_gemms_only(acts, outs, resident), args.steps)
@@ -278,11 +280,16 @@ def run_stack(args) -> int:
             fm, fx, fy, fws = runner.fused_inputs(batch)
             t_fused = timed(lambda: runner.run_fused(fm, fx, fy, fws), args.steps)
             del fx, fy, fws
+        tx, ty, tws = runner.tiled_inputs(batch)
+        t_tiled = timed(lambda: runner.run_fused_tiled(tx, ty, tws), args.steps)
+        del tx, ty, tws
         res[f"batch{batch}"] = {
             "forward_ms": {"decode_only": round(t_dec, 4), "bf16_gemm_only": round(t_gemm, 4),
                            "df11_serial": round(t_ser, 4),
+                           "df11_fused_tiled": round(t_tiled, 4),
                            "df11_overlapped_by_decode_groups": {str(g): round(t, 4)
                                                                 for g, t in t_ovl.items()}},
+            "df11_fused_tiled_over_bf16": round(t_tiled / t_gemm, 4),
             "decode_over_gemm": round(t_dec / t_gemm, 4),
             "df11_serial_over_bf16": round(t_ser / t_gemm, 4),
             "df11_overlapped_over_bf16": round(t_ovl[best] / t_gemm, 4),
@@ -473,6 +480,8 @@ def main() -> int:
                     help="rotating encoded copies and output buffers (0: enough that they "
                          "span at least 768 MB, three times the 256 MB Infinity Cache, and "
                          "at least 3)")
+    ap.add_argument("--max-groups", type=int, default=0,
+                    help="cap on the decode's workgroups (0: as many as fit on the GPU)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-gemm", action="store_true", help="skip the decode/GEMM ratios")
     ap.add_argument("--mode", choices=("decode", "copy", "stack", "encode", "offload", "ceiling"),
@@ -527,6 +536,8 @@ def main() -> int:
     # nothing of its bytes in the 256 MB Infinity Cache from the launch before
     n_copies = args.copies or max(3, -(-768_000_000 // (rd + wr)))
     copies = [hd.to_device(enc, dev) for _ in range(n_copies)]
+    for c in copies:
+        c.desc.max_groups = args.max_groups
     outs = [torch.empty(n, dtype=torch.bfloat16, device=dev) for _ in range(n_copies)]
     stream = torch.cuda.current_stream(dev)
 
@@ -609,7 +620,7 @@ def main() -> int:
                    "total_code_bits": int(enc.sizes.total_bits),
                    "max_code_len": int(enc.codebook.max_len),
                    "n_tables": int(enc.codebook.n_tables),
-                   "rotating_copies": n_copies,
+                   "rotating_copies": n_copies, "max_groups": args.max_groups,
                    "resident_bytes_rotated": n_copies * (rd + wr),
                    "host_encode_s": round(t_enc, 2)},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,

@@ -16,15 +16,18 @@ from __future__ import annotations
 
 from dataclasses import dataclass
 
-from . import DeviceEncoded, df11_decode, df11_decode_gemm, df11_gemm_workspace_bytes, gemv_matrices
+from . import (DeviceEncoded, TiledDevice, df11_decode, df11_decode_gemm, df11_decode_gemm_tiled,
+               df11_gemm_workspace_bytes, df11_tiled_workspace_bytes, gemv_matrices)
 
 
 @dataclass
 class StackBlock:
     """One encoded transformer block and the (rows, cols) of its matrices in
-    storage order (row-major, concatenated)."""
+    storage order (row-major, concatenated); optionally the same block
+    encoded in operand-tile order for the tiled product."""
     dev: DeviceEncoded
     shapes: list[tuple[int, int]]
+    tiled: TiledDevice | None = None
 
 
 class StackRunner:
@@ -152,6 +155,29 @@ class StackRunner:
         s = self.compute_stream
         for i, blk in enumerate(self.blocks):
             df11_decode_gemm(blk.dev, mats[i], x, y, ws, s)
+
+
+    def tiled_inputs(self, batch: int, seed: int = 4002):
+        """Inputs, outputs and workspace for run_fused_tiled (every block must
+        carry its tile-order encoding)."""
+        import torch
+        if any(b.tiled is None for b in self.blocks):
+            raise ValueError("run_fused_tiled needs every block's tile-order encoding")
+        nx = max(max(m.x_offset + m.cols for m in b.tiled.mats) for b in self.blocks)
+        ny = max(sum(m.rows for m in b.tiled.mats) for b in self.blocks)
+        g = torch.Generator(device=self.device).manual_seed(seed)
+        x = torch.randn(batch, nx, generator=g, device=self.device).to(torch.bfloat16)
+        y = torch.empty(batch, ny, dtype=torch.float32, device=self.device)
+        need = max(df11_tiled_workspace_bytes(b.tiled.mats, batch) for b in self.blocks)
+        ws = torch.empty(need, dtype=torch.uint8, device=self.device) if need else None
+        return x, y, ws
+
+    def run_fused_tiled(self, x, y, ws):
+        """y = W x for every block on the matrix cores, straight from its
+        tile-order stream (no BF16 weights anywhere)."""
+        s = self.compute_stream
+        for blk in self.blocks:
+            df11_decode_gemm_tiled(blk.tiled, x, y, ws, s)
 
 
 class OffloadRunner:

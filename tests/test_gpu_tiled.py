@@ -236,3 +236,25 @@ def test_tiled_corrupt_blocks_stay_contained(torch):
                 checked += 1
             seg += 1
     assert checked > 0
+
+
+def test_stack_runner_fused_tiled(torch):
+    """The stack schedule of the tiled product: every block writes the same y
+    (one activation buffer), so after a pass y holds the last block's result,
+    which must equal a direct call on that block bit for bit."""
+    from huffman_decode_amd.pipeline import StackBlock, StackRunner
+    blocks = []
+    for layer in range(3):
+        w = wl.llama8b_block(seed=(3001, layer), scale=1 / 64)
+        shapes = [(m.rows, m.cols) for m in w.matrices]
+        te = hd.encode_tiled(w.weights, shapes)
+        blocks.append(StackBlock(hd.to_device(hd.encode(w.weights)), shapes, hd.tiled_to_device(te)))
+    runner = StackRunner(blocks)
+    for batch in (4, 24):
+        x, y, ws = runner.tiled_inputs(batch)
+        _say(f"[gpu] stack runner fused tiled batch={batch}")
+        runner.run_fused_tiled(x, y, ws)
+        y_ref = torch.empty_like(y)
+        hd.df11_decode_gemm_tiled(blocks[-1].tiled, x, y_ref, ws)
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int32), y_ref.view(torch.int32))
