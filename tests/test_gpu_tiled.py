@@ -258,3 +258,27 @@ def test_stack_runner_fused_tiled(torch):
         hd.df11_decode_gemm_tiled(blocks[-1].tiled, x, y_ref, ws)
         torch.cuda.synchronize()
         assert torch.equal(y.view(torch.int32), y_ref.view(torch.int32))
+
+
+def test_stream_ceiling_reads_every_byte(torch):
+    """The traffic-only kernel the decode is measured against: out word i of
+    group g is sign|mantissa byte i of that group widened to 16 bits, XORed
+    with b's 16-byte unit of the group (units spread evenly over the groups)."""
+    n, b_bytes = 8 * 3001, 16 * 257
+    rng = np.random.default_rng(71)
+    a = rng.integers(0, 256, n).astype(np.uint8)
+    b = rng.integers(0, 256, b_bytes).astype(np.uint8)
+    out = torch.full((n + 8,), 0x1234, dtype=torch.int16, device="cuda")
+    _say("[gpu] df11_stream_ceiling")
+    hd.df11_stream_ceiling(torch.from_numpy(a).cuda(), torch.from_numpy(b).cuda(), out, n)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().view(np.uint16)
+    assert np.all(got[n:] == 0x1234), "wrote past the output"
+    groups, units = n // 8, b_bytes // 16
+    want = a.astype(np.uint16).reshape(groups, 8).copy()
+    bw = b.view(np.uint16).reshape(units, 8)
+    for g in range(groups):
+        u0, u1 = g * units // groups, (g + 1) * units // groups
+        if u0 < u1:
+            want[g] ^= bw[u0]
+    assert np.array_equal(got[:n].reshape(groups, 8), want)
