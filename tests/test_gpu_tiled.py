@@ -261,9 +261,12 @@ def test_stack_runner_fused_tiled(torch):
 
 
 def test_stream_ceiling_reads_every_byte(torch):
-    """The traffic-only kernel the decode is measured against: out word i of
-    group g is sign|mantissa byte i of that group widened to 16 bits, XORed
-    with b's 16-byte unit of the group (units spread evenly over the groups)."""
+    """The traffic-only kernel the decode is measured against.  A wave takes
+    tiles of 128 consecutive 8-word groups, lane l groups l and l + 64 of the
+    tile; tile t's share of b is its 16-byte units [t U / T, (t + 1) U / T),
+    lane l XORing units l, l + 64, ... of that share into both its groups.
+    Each output word is its sign|mantissa byte widened to 16 bits, XORed with
+    the lane's share."""
     n, b_bytes = 8 * 3001, 16 * 257
     rng = np.random.default_rng(71)
     a = rng.integers(0, 256, n).astype(np.uint8)
@@ -275,10 +278,16 @@ def test_stream_ceiling_reads_every_byte(torch):
     got = out.cpu().numpy().view(np.uint16)
     assert np.all(got[n:] == 0x1234), "wrote past the output"
     groups, units = n // 8, b_bytes // 16
+    tiles = -(-groups // 128)
     want = a.astype(np.uint16).reshape(groups, 8).copy()
     bw = b.view(np.uint16).reshape(units, 8)
-    for g in range(groups):
-        u0, u1 = g * units // groups, (g + 1) * units // groups
-        if u0 < u1:
-            want[g] ^= bw[u0]
+    for t in range(tiles):
+        u0, u1 = t * units // tiles, (t + 1) * units // tiles
+        for lane in range(64):
+            extra = np.zeros(8, np.uint16)
+            for u in range(u0 + lane, u1, 64):
+                extra ^= bw[u]
+            for g in (128 * t + lane, 128 * t + 64 + lane):
+                if g < groups:
+                    want[g] ^= extra
     assert np.array_equal(got[:n].reshape(groups, 8), want)
