@@ -193,9 +193,40 @@ def launch_time_ms(launch, stream, reps=20, warmup=100) -> float:
     return a.elapsed_time(b) / reps
 
 
-def gemm_ratios(wlx, out, decode_ms, stream, batches=(1, 2, 4, 16, 64), reps=10) -> dict:
+def captured(fn, outputs=None, replays=3):
+    """fn() captured in a HIP graph (torch.cuda.CUDAGraph), so that its many
+    small launches replay with no host overhead in between.  Returns the
+    graph.  The graph is used only if it gives what the eager calls give:
+    the outputs (those passed, else the tensors fn returns) are overwritten
+    with a byte pattern before each of a few replays, with the program's own
+    work in between, and must then equal an eager run's."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        eager = fn()  # also warms the libraries outside the capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    expect = [t.clone() for t in (outputs if outputs is not None else eager)]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        outs = fn()
+    outs = list(outputs if outputs is not None else outs)
+    for _ in range(replays):
+        for t in outs:
+            t.view(torch.uint8).fill_(0xA5)
+        graph.replay()
+        torch.cuda.synchronize()
+        if not all(torch.equal(a, e) for a, e in zip(outs, expect)):
+            raise RuntimeError("a captured graph's replay differs from the eager result")
+    return graph
+
+
+def gemm_ratios(wlx, out, decode_ms, stream, batches=(1, 2, 4, 16, 64), reps=20) -> dict:
     """Decode time of the block over the time of the block's bf16 GEMMs
-    (y = x W^T for each of its matrices, on the decoded weights) at each batch."""
+    (y = x W^T for each of its matrices, on the decoded weights) at each batch.
+    The 7 GEMMs of a batch are replayed as one HIP graph: launched one by one
+    from Python they would partly measure the host (about 20 us per GEMM)."""
     import torch
     res = {}
     mats, off = [], 0
@@ -207,23 +238,26 @@ def gemm_ratios(wlx, out, decode_ms, stream, batches=(1, 2, 4, 16, 64), reps=10)
         xs = [torch.randn(b, w.shape[1], device=out.device, generator=g).to(torch.bfloat16)
               for w in mats]
 
-        def block_gemms(_k):
-            for x, w in zip(xs, mats):
-                torch.nn.functional.linear(x, w)
-        gms = launch_time_ms(block_gemms, stream, reps)
+        def block_gemms():
+            return [torch.nn.functional.linear(x, w) for x, w in zip(xs, mats)]
+        graph = captured(block_gemms)
+        gms = launch_time_ms(lambda _k: graph.replay(), stream, reps)
         # bytes a BF16 GEMM moves: the weights, x and y (bf16)
         moved = sum(2 * w.numel() + 2 * b * (w.shape[0] + w.shape[1]) for w in mats)
         res[f"batch{b}"] = {"gemm_ms": round(gms, 5), "decode_over_gemm": round(decode_ms / gms, 4),
                             "gemm_gbs": round(moved / (gms * 1e-3) / 1e9, 1)}
+        del graph
     return res
 
 
 def run_stack(args) -> int:
     """The 32-block Llama-3.1-8B-shaped stack: each block decoded into a reused
-    BF16 buffer, then its 7 bf16 GEMMs at batch 1 and 64.  Reports the time of
-    one forward pass (all blocks) for the decodes alone, the GEMMs alone on
-    resident BF16 weights, decode+GEMMs on one stream, and decode of block i+1
-    overlapped with the GEMMs of block i on two streams; and their ratios."""
+    BF16 buffer, then its 7 bf16 GEMMs, at batches 1, 4, 16 and 64.  Reports
+    the time of one forward pass (all blocks) for the decodes alone, the GEMMs
+    alone on resident BF16 weights, decode+GEMMs on one stream, decode of
+    block i+1 overlapped with the GEMMs of block i on two streams, and the
+    fused products; and their ratios.  Single-stream schedules run as
+    captured HIP graphs."""
     import numpy as np
     import torch
     import huffman_decode_amd as hd
@@ -265,12 +299,25 @@ def run_stack(args) -> int:
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / reps
 
+    # Single-stream schedules are replayed as HIP graphs (hundreds of small
+    # launches per forward pass would otherwise partly time the host); each
+    # graph's replays are checked against the eager outputs first.  The
+    # two-stream overlapped schedule runs eagerly.
+    def graphed(fn, outputs):
+        g = captured(fn, outputs)
+        return lambda: g.replay(), g
+
     res = {}
     for batch in (1, 4, 16, 64):
         acts, outs = runner.activations(batch)
-        t_dec = timed(runner.run_decodes_only, args.steps)
-        t_gemm = timed(lambda: runner.run_gemms_only(acts, outs, resident), args.steps)
-        t_ser = timed(lambda: runner.run_serial(acts, outs), args.steps)
+        outs_list = list(outs.values())
+        run, g1 = graphed(runner.run_decodes_only, runner.buffers)
+        t_dec = timed(run, args.steps)
+        run, g2 = graphed(lambda: runner.run_gemms_only(acts, outs, resident), outs_list)
+        t_gemm = timed(run, args.steps)
+        run, g3 = graphed(lambda: runner.run_serial(acts, outs), outs_list)
+        t_ser = timed(run, args.steps)
+        del g1, g2, g3
         t_ovl = {g: timed(lambda: runner.run_overlapped(acts, outs, g), args.steps)
                  for g in (0, 512, 384, 256)}
         best = min(t_ovl, key=t_ovl.get)
@@ -278,11 +325,13 @@ def run_stack(args) -> int:
         t_fused = None
         if batch <= 4:
             fm, fx, fy, fws = runner.fused_inputs(batch)
-            t_fused = timed(lambda: runner.run_fused(fm, fx, fy, fws), args.steps)
-            del fx, fy, fws
+            run, g4 = graphed(lambda: runner.run_fused(fm, fx, fy, fws), [fy])
+            t_fused = timed(run, args.steps)
+            del fx, fy, fws, g4
         tx, ty, tws = runner.tiled_inputs(batch)
-        t_tiled = timed(lambda: runner.run_fused_tiled(tx, ty, tws), args.steps)
-        del tx, ty, tws
+        run, g5 = graphed(lambda: runner.run_fused_tiled(tx, ty, tws), [ty])
+        t_tiled = timed(run, args.steps)
+        del tx, ty, tws, g5
         res[f"batch{batch}"] = {
             "forward_ms": {"decode_only": round(t_dec, 4), "bf16_gemm_only": round(t_gemm, 4),
                            "df11_serial": round(t_ser, 4),

@@ -47,7 +47,13 @@ class StackRunner:
         self.buffers = [torch.empty(n_max, dtype=torch.bfloat16, device=self.device)
                         for _ in range(2)]
         self.decode_stream = torch.cuda.Stream(device=self.device)
-        self.compute_stream = torch.cuda.current_stream(self.device)
+
+    @property
+    def compute_stream(self):
+        """torch's current stream on the device, read at each call (so that
+        a schedule run under a HIP graph capture is captured)."""
+        import torch
+        return torch.cuda.current_stream(self.device)
 
     @staticmethod
     def _views(buf, shapes):
@@ -227,7 +233,13 @@ class OffloadRunner:
         self.buffers = [torch.empty(n_max, dtype=torch.bfloat16, device=self.device)
                         for _ in range(2)]
         self.copy_stream = torch.cuda.Stream(device=self.device)
-        self.compute_stream = torch.cuda.current_stream(self.device)
+
+    @property
+    def compute_stream(self):
+        """torch's current stream on the device, read at each call (so that
+        a schedule run under a HIP graph capture is captured)."""
+        import torch
+        return torch.cuda.current_stream(self.device)
 
     def _desc(self, i, slot):
         enc = self.encoded[i]
