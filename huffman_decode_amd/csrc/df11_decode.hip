@@ -1208,14 +1208,6 @@ __device__ __forceinline__ BlockIn load_block(const DecodeArgs &a, uint32_t blk,
     return r;
 }
 
-// The lane's 8 sign|mantissa bytes of operand tile tt, if its group holds a
-// word of [w_lo, w_hi) (zero otherwise, and nothing is read).
-__device__ __forceinline__ uint2 tile_sm(const uint8_t *signmant, uint32_t tt, uint32_t w_lo,
-                                         uint32_t w_hi, uint32_t lane) {
-    const uint32_t q = (tt << 9) + 8 * lane;
-    return q + 8 > w_lo && q < w_hi ? load_sm8(signmant + q) : make_uint2(0, 0);
-}
-
 // Where the lane's B operands come from: vector 16 nt + lane % 16 of the
 // batch, inputs xl + 16 nt x_stride + 32 ks + 0..7 for k-step ks (xl already
 // holds the lane's vector, the matrix's x offset and the lane's 8 columns).
@@ -1236,15 +1228,32 @@ __device__ __forceinline__ void tile_x(u32x4 (&bv)[NT], const XSrc &xs, uint32_t
                      : u32x4{0, 0, 0, 0};
 }
 
-// The lane's A operand of operand tile tt: its 8 words (exponents at LDS tile
-// byte q - t_base, sign|mantissa bytes sm), those outside [w_lo, w_hi) zero.
-__device__ __forceinline__ u32x4 tile_a(const uint8_t *tile, uint32_t t_base, uint2 sm, uint32_t tt,
-                                        uint32_t w_lo, uint32_t w_hi, uint32_t lane) {
-    const uint32_t q = (tt << 9) + 8 * lane;
+// The lane's 8 exponent bytes of the group at word q (rotated, as in LDS):
+// words at or after `split` from the LDS tile (the word at q at byte q -
+// t_base), those before it from `carry` (what the wave's previous blocks
+// decoded of the same operand tile).  The tile is read only for a group that
+// holds words of [split, hi): q >= t_base then holds, since t_base is split
+// rounded down to 8, and q - t_base stays inside the block's decoded range.
+__device__ __forceinline__ uint2 tile_exps(const uint8_t *tile, uint32_t t_base, uint32_t q,
+                                           uint32_t split, uint32_t hi, uint2 carry) {
+    if (q + 8 <= split || q >= hi) return carry;
+    const uint2 t = *reinterpret_cast<const uint2 *>(tile + (q - t_base));
+    if (q >= split) return t;
+    // bytes [0, k) from carry, [k, 8) from the tile (0 < k < 8)
+    const uint64_t keep = (1ull << (8 * (split - q))) - 1;
+    const uint64_t c64 = ((uint64_t)carry.y << 32) | carry.x, t64 = ((uint64_t)t.y << 32) | t.x;
+    const uint64_t m = (c64 & keep) | (t64 & ~keep);
+    return make_uint2((uint32_t)m, (uint32_t)(m >> 32));
+}
+
+// The lane's A operand of the group at word q: its 8 words joined from
+// exponent bytes e and sign|mantissa bytes sm, those outside [w_lo, w_hi)
+// zero.
+__device__ __forceinline__ u32x4 tile_a(uint2 e, uint2 sm, uint32_t q, uint32_t w_lo, uint32_t w_hi) {
     const uint32_t lo = q > w_lo ? q : w_lo, hi = q + 8 < w_hi ? q + 8 : w_hi;
     u32x4 av = {0, 0, 0, 0};
     if (lo < hi) {
-        const uint4 w = join8(*reinterpret_cast<const uint2 *>(tile + (q - t_base)), sm);
+        const uint4 w = join8(e, sm);
         av = u32x4{w.x, w.y, w.z, w.w};
         if (hi - lo < 8) {
             const uint32_t a0 = lo - q, a1 = hi - q;  // words [a0, a1) are kept
@@ -1267,19 +1276,78 @@ __device__ __forceinline__ void tile_mfma(f32x4 (&acc)[NT], u32x4 av, const u32x
                                                           acc[nt], 0, 0, 0);
 }
 
-// Multiply the operand tiles that words [w_lo, w_hi) of the decoded block
-// reach (each word's exponent at LDS tile byte q - t_base) into acc.
+// One operand tile tt into acc: words [w_lo, w_hi) of it, exponent bytes as
+// tile_exps gives them.
+// (kMerge false: no word of the tile lies before split.)
+template <int NT, bool kMerge>
+__device__ __forceinline__ void tile_step(uint32_t tt, uint32_t w_lo, uint32_t w_hi, uint32_t split,
+                                          uint32_t t_base, const uint8_t *tile,
+                                          const uint8_t *signmant, const XSrc &xs, uint32_t seg_tile,
+                                          uint32_t lane, uint2 carry, f32x4 (&acc)[NT]) {
+    u32x4 bv[NT];
+    tile_x<NT>(bv, xs, tt - seg_tile);
+    const uint32_t q = (tt << 9) + 8 * lane;
+    const uint2 sm = q + 8 > w_lo && q < w_hi ? load_sm8(signmant + q) : make_uint2(0, 0);
+    uint2 e;
+    if (kMerge)
+        e = tile_exps(tile, t_base, q, split, w_hi, carry);
+    else
+        e = q < w_hi ? *reinterpret_cast<const uint2 *>(tile + (q - t_base)) : make_uint2(0, 0);
+    tile_mfma<NT>(acc, tile_a(e, sm, q, w_lo, w_hi), bv);
+}
+
+// An operand tile wholly inside the block's decoded words: no masks.
 template <int NT>
-__device__ __forceinline__ void mfma_window(uint32_t w_lo, uint32_t w_hi, uint32_t t_base,
-                                            const uint8_t *tile, const uint8_t *signmant,
-                                            const XSrc &xs, uint32_t seg_tile, uint32_t lane,
+__device__ __forceinline__ void tile_whole(uint32_t tt, uint32_t t_base, const uint8_t *tile,
+                                           const uint8_t *signmant, const XSrc &xs, uint32_t seg_tile,
+                                           uint32_t lane, f32x4 (&acc)[NT]) {
+    u32x4 bv[NT];
+    tile_x<NT>(bv, xs, tt - seg_tile);
+    const uint32_t q = (tt << 9) + 8 * lane;
+    const uint4 w = join8(*reinterpret_cast<const uint2 *>(tile + (q - t_base)),
+                          load_sm8(signmant + q));
+    tile_mfma<NT>(acc, u32x4{w.x, w.y, w.z, w.w}, bv);
+}
+
+// Multiply the operand tiles that words [w_lo, w_hi) reach into acc.  Words
+// [w_lo, split) were decoded by the wave's earlier blocks and sit in carry
+// (they share the first tile); words [split, w_hi) are this block's, in the
+// LDS tile (word q at byte q - t_base).  With `defer` the last tile, which
+// the wave's next block completes, is not multiplied: its exponent bytes go
+// to carry instead.
+template <int NT>
+__device__ __forceinline__ void mfma_window(uint32_t w_lo, uint32_t split, uint32_t w_hi,
+                                            bool defer, uint32_t t_base, const uint8_t *tile,
+                                            const uint8_t *signmant, const XSrc &xs,
+                                            uint32_t seg_tile, uint32_t lane, uint2 &carry,
                                             f32x4 (&acc)[NT]) {
-    for (uint32_t tt = w_lo >> 9; tt < (w_hi + 511) >> 9; ++tt) {
-        u32x4 bv[NT];
-        tile_x<NT>(bv, xs, tt - seg_tile);
-        const uint2 sm = tile_sm(signmant, tt, w_lo, w_hi, lane);
-        tile_mfma<NT>(acc, tile_a(tile, t_base, sm, tt, w_lo, w_hi, lane), bv);
+    uint32_t tt = w_lo >> 9;
+    const uint32_t t_end = defer ? w_hi >> 9 : (w_hi + 511) >> 9;
+    if (tt < t_end) {  // the first tile: carried words merged
+        tile_step<NT, true>(tt, w_lo, w_hi, split, t_base, tile, signmant, xs, seg_tile, lane, carry,
+                            acc);
+        // the block's later tiles (split lies below them): whole ones, then a
+        // last partial one
+        for (++tt; tt < (w_hi >> 9); ++tt)
+            tile_whole<NT>(tt, t_base, tile, signmant, xs, seg_tile, lane, acc);
+        if (tt < t_end) {
+            tile_step<NT, false>(tt, w_lo, w_hi, split, t_base, tile, signmant, xs, seg_tile, lane,
+                                 carry, acc);
+            ++tt;
+        }
     }
+    if (defer) carry = tile_exps(tile, t_base, (tt << 9) + 8 * lane, split, w_hi, carry);
+}
+
+// The carried words [c_lo, c_hi) alone (the wave's next block does not go on
+// with them).
+template <int NT>
+__device__ __forceinline__ void flush_carry(uint32_t c_lo, uint32_t c_hi, const uint8_t *signmant,
+                                            const XSrc &xs, uint32_t seg_tile, uint32_t lane,
+                                            uint2 carry, f32x4 (&acc)[NT]) {
+    // split past the window: every exponent byte from carry, no LDS read
+    tile_step<NT, true>(c_lo >> 9, c_lo, c_hi, 0xFFFFFFFFu, 0u, nullptr, signmant, xs, seg_tile,
+                        lane, carry, acc);
 }
 
 // Input ranges for df11_tile_inputs_kernel: range r is x[b * x_stride +
@@ -1320,7 +1388,7 @@ __global__ __launch_bounds__(256) void df11_tile_inputs_kernel(TileInputs t) {
 // Occupancy: up to 32 vectors the decode's 80-VGPR budget (3 workgroups per
 // CU); 64 vectors 128 VGPRs (2 per CU).
 template <int NT> struct TiledOccupancy {
-    static constexpr int kValue = NT <= 2 ? kWavesPerEu : 4;
+    static constexpr int kValue = NT == 1 ? 8 : NT == 2 ? kWavesPerEu : 4;
 };
 
 template <int NT>
@@ -1388,8 +1456,12 @@ void df11_tiled_kernel(DecodeArgs a, TiledArgs t) {
     if (lut_one_load && threadIdx.x < lut_u4_count) lv = a.luts[threadIdx.x];
     const uint4 *dec_src = a.luts + lut_u4_count;
     const uint4 dv0 = dec_src[threadIdx.x], dv1 = dec_src[threadIdx.x + kGroupThreads];
-    uint32_t b = blk_lo + wave;
-    BlockIn nxt = load_block(a, b <= blk_hi ? b : blk_hi, lane);
+    // the wave's run of consecutive blocks [b, r_hi): an operand tile that a
+    // block leaves unfinished is completed by the next block of the run
+    const uint32_t nb = blk_hi + 1 - blk_lo;
+    uint32_t b = blk_lo + wave * nb / kWavesPerGroup;
+    const uint32_t r_hi = blk_lo + (wave + 1) * nb / kWavesPerGroup;
+    BlockIn nxt = load_block(a, b, lane);
     uint4 *lut_u4 = reinterpret_cast<uint4 *>(lut);
     if (lut_one_load) {
         if (threadIdx.x < lut_u4_count) lut_u4[threadIdx.x] = lv;
@@ -1404,9 +1476,12 @@ void df11_tiled_kernel(DecodeArgs a, TiledArgs t) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     const uint32_t gap_shift = (5 * lane) & 31;
-    for (; b <= blk_hi; b += kWavesPerGroup) {
+    // carried words [c_lo, c_hi) of one operand tile (c_hi == c_lo: none)
+    uint2 carry = make_uint2(0, 0);
+    uint32_t c_lo = 0, c_hi = 0;
+    for (; b < r_hi; ++b) {
         const BlockIn cur = nxt;
-        if (b + kWavesPerGroup <= blk_hi) nxt = load_block(a, b + kWavesPerGroup, lane);
+        if (b + 1 < r_hi) nxt = load_block(a, b + 1, lane);
         const uint32_t p0 = __builtin_amdgcn_readlane(cur.pos, 0);
         const uint32_t p1 = __builtin_amdgcn_readlane(cur.pos, 1);
         const bool sane = p1 >= p0 && p1 <= a.n && p1 - p0 <= (uint32_t)kMaxBlockCodes;
@@ -1450,6 +1525,8 @@ void df11_tiled_kernel(DecodeArgs a, TiledArgs t) {
         const uint32_t total = __builtin_amdgcn_readlane(incl, kWave - 1);
         if (!sane || total != p1 - p0) {  // a corrupt block: reported, its words left out
             if (lane == 0 && a.status) atomicAdd(a.status, 1u);
+            if (c_lo < c_hi) flush_carry<NT>(c_lo, c_hi, a.signmant, xs, seg_tile, lane, carry, acc);
+            c_hi = c_lo;
             wave_lds_sync();
             continue;
         }
@@ -1473,11 +1550,25 @@ void df11_tiled_kernel(DecodeArgs a, TiledArgs t) {
                          tile_addr + at);
             wave_lds_sync();
         }
+        // the carried words go on at w_lo (a run's blocks are consecutive)
+        const bool go_on = c_lo < c_hi && c_hi == w_lo && w_lo < w_hi;
+        if (c_lo < c_hi && !(go_on && one_pass))
+            flush_carry<NT>(c_lo, c_hi, a.signmant, xs, seg_tile, lane, carry, acc);
         if (one_pass) {
-            if (w_lo < w_hi)
-                mfma_window<NT>(w_lo, w_hi, base, tile, a.signmant, xs, seg_tile, lane, acc);
+            if (w_lo < w_hi) {
+                // leave the last tile to the next block if that block completes it
+                const bool defer = b + 1 < r_hi && (w_hi & 511u) != 0;
+                const uint32_t lo = go_on ? c_lo : w_lo;
+                mfma_window<NT>(lo, w_lo, w_hi, defer, base, tile, a.signmant, xs, seg_tile, lane,
+                                carry, acc);
+                c_lo = defer ? (lo > ((w_hi - 1) & ~511u) ? lo : (w_hi - 1) & ~511u) : 0u;
+                c_hi = defer ? w_hi : 0u;
+            } else {
+                c_lo = c_hi = 0;
+            }
             wave_lds_sync();
         } else {
+            c_lo = c_hi = 0;
             // more symbols than one tile holds: decode again per tile-sized window
             for (uint32_t r0 = 0; r0 < groups * 8; r0 += kTileCap) {
                 decode_codes<true>(lds_dec, lut, a.n_tables, cur.d0, cur.d1, cur.d2, start, lim,
@@ -1486,7 +1577,8 @@ void df11_tiled_kernel(DecodeArgs a, TiledArgs t) {
                 const uint32_t r_lo = base + r0, r_hi = base + r0 + kTileCap;
                 const uint32_t v_lo = w_lo > r_lo ? w_lo : r_lo, v_hi = w_hi < r_hi ? w_hi : r_hi;
                 if (v_lo < v_hi)
-                    mfma_window<NT>(v_lo, v_hi, r_lo, tile, a.signmant, xs, seg_tile, lane, acc);
+                    mfma_window<NT>(v_lo, v_lo, v_hi, false, r_lo, tile, a.signmant, xs, seg_tile,
+                                    lane, carry, acc);
                 wave_lds_sync();
             }
         }
