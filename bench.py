@@ -424,7 +424,7 @@ def fused_gemm(wlx, copies, stream, batch, reps=20) -> dict:
     return {"fused_ms": round(ms, 5)}
 
 
-def fused_tiled(wlx, stream, batches, n_copies=3, reps=20) -> dict:
+def fused_tiled(wlx, stream, batches, n_copies=3, reps=20, warmup=100) -> dict:
     """y_b = W x_b for `batch` vectors on the matrix cores from the block
     encoded in operand-tile order (df11_decode_gemm_tiled), timed over
     back-to-back launches on rotating copies like the decode."""
@@ -445,11 +445,28 @@ def fused_tiled(wlx, stream, batches, n_copies=3, reps=20) -> dict:
         need = hd.df11_tiled_workspace_bytes(te.mats, batch)
         ws = torch.empty(need, dtype=torch.uint8, device="cuda") if need else None
         ms = launch_time_ms(lambda k: hd.df11_decode_gemm_tiled(copies[k % n_copies], x, y, ws,
-                                                                stream), stream, reps)
+                                                                stream), stream, reps, warmup)
         res[f"batch{batch}"] = {"fused_ms": round(ms, 5),
                                 "fused_gbs": round((rd + 2 * batch * nx + 4 * batch * ny)
                                                    / (ms * 1e-3) / 1e9, 1)}
     return res
+
+
+def run_tiled(args) -> int:
+    """Only the tiled product (df11_decode_gemm_tiled) on the workload at each
+    of --batches, with --warmup and --steps launches (a short run for counter
+    collection)."""
+    import torch
+    from huffman_decode_amd import workloads as wl
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wlx = wl.CONFIGS[args.workload]()
+    batches = [int(b) for b in args.batches.split(",")]
+    res = fused_tiled(wlx, torch.cuda.current_stream(dev), batches, reps=args.steps,
+                      warmup=args.warmup)
+    print(json.dumps({"mode": "tiled", "workload": args.workload, "steps": args.steps,
+                      "warmup": args.warmup, **res}), flush=True)
+    return 0
 
 
 def run_offload(args) -> int:
@@ -533,14 +550,17 @@ def main() -> int:
                     help="cap on the decode's workgroups (0: as many as fit on the GPU)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-gemm", action="store_true", help="skip the decode/GEMM ratios")
-    ap.add_argument("--mode", choices=("decode", "copy", "stack", "encode", "offload", "ceiling"),
+    ap.add_argument("--mode", choices=("decode", "copy", "stack", "encode", "offload", "ceiling",
+                                       "tiled"),
                     default="decode",
                     help="ceiling: only the traffic-only kernel on the workload's bytes; "
+                         "tiled: only the tiled product at --batches; "
                          "copy: time a plain device copy of --copy-mib MiB instead; "
                          "stack: decode/GEMM schedules over the 32-block 8B-shaped stack; "
                          "encode: host encoder throughput (no GPU); "
                          "offload: blocks from pinned host memory, copied and decoded in turn")
     ap.add_argument("--layers", type=int, default=32, help="blocks in the stack mode")
+    ap.add_argument("--batches", default="1,16,64", help="vectors per call in the tiled mode")
     ap.add_argument("--copy-mib", type=int, default=1024)
     args = ap.parse_args()
     fast = args.mode in ("decode", "copy", "ceiling")
@@ -563,6 +583,8 @@ def main() -> int:
         return run_encode(args)
     if args.mode == "offload":
         return run_offload(args)
+    if args.mode == "tiled":
+        return run_tiled(args)
 
     import numpy as np
     import torch
