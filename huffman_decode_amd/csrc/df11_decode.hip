@@ -1211,21 +1211,45 @@ __device__ __forceinline__ BlockIn load_block(const DecodeArgs &a, uint32_t blk,
 // Where the lane's B operands come from: vector 16 nt + lane % 16 of the
 // batch, inputs xl + 16 nt x_stride + 32 ks + 0..7 for k-step ks (xl already
 // holds the lane's vector, the matrix's x offset and the lane's 8 columns).
+// (One vector: xl is the matrix's inputs, and the inputs of k-steps [ks0,
+// ks0 + 4) are held across the wave, two per lane (lane l: columns 32 ks0 +
+// 2 l and + 1), in xw.)
 struct XSrc {
     const g_cu16 *xl;       // the lane's 8 inputs of group 0, k-step 0
     uint64_t group_stride;  // from one group of 16 vectors to the next
     uint64_t ks_stride;     // from one k-step to the next
     uint32_t live;          // vectors of the lane's column below the batch: bit nt
+    uint32_t ks0, xw, cols;
 };
 
 // The lane's B operands of k-step ks: 8 inputs of vector 16 nt + lane % 16.
-template <int NT>
-__device__ __forceinline__ void tile_x(u32x4 (&bv)[NT], const XSrc &xs, uint32_t ks) {
+// kX1 (one vector): gathered from the four k-steps held in xw (every lane
+// gets vector 0's inputs of its column group: the extra columns of the
+// product are never written out); a k-step outside them loads the next four.
+template <int NT, bool kX1>
+__device__ __forceinline__ void tile_x(u32x4 (&bv)[NT], XSrc &xs, uint32_t ks) {
+    if constexpr (kX1) {
+        if (ks - xs.ks0 >= 4u) {  // rare: a block reaching past its window's first 4 k-steps
+            xs.ks0 = ks;
+            uint32_t col = 32 * ks + 2 * (threadIdx.x % 64);
+            col = col < xs.cols - 2 ? col : xs.cols - 2;
+            xs.xw = *(const __attribute__((address_space(1))) uint32_t *)(xs.xl + col);
+            // wait here, so that the common path, where this branch joins it,
+            // carries no load in flight into its next wait
+            __builtin_amdgcn_s_waitcnt(0);
+        }
+        const int at = (int)(64 * (ks - xs.ks0) + 16 * ((threadIdx.x % 64) / 16));
+        bv[0] = u32x4{(uint32_t)__builtin_amdgcn_ds_bpermute(at, (int)xs.xw),
+                      (uint32_t)__builtin_amdgcn_ds_bpermute(at + 4, (int)xs.xw),
+                      (uint32_t)__builtin_amdgcn_ds_bpermute(at + 8, (int)xs.xw),
+                      (uint32_t)__builtin_amdgcn_ds_bpermute(at + 12, (int)xs.xw)};
+    } else {
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
-        bv[nt] = (xs.live >> nt) & 1u
-                     ? *(const g_cu32x4 *)(xs.xl + nt * xs.group_stride + ks * xs.ks_stride)
-                     : u32x4{0, 0, 0, 0};
+        for (int nt = 0; nt < NT; ++nt)
+            bv[nt] = (xs.live >> nt) & 1u
+                         ? *(const g_cu32x4 *)(xs.xl + nt * xs.group_stride + ks * xs.ks_stride)
+                         : u32x4{0, 0, 0, 0};
+    }
 }
 
 // The lane's 8 exponent bytes of the group at word q (rotated, as in LDS):
@@ -1279,15 +1303,19 @@ __device__ __forceinline__ void tile_mfma(f32x4 (&acc)[NT], u32x4 av, const u32x
 // One operand tile tt into acc: words [w_lo, w_hi) of it, exponent bytes as
 // tile_exps gives them.
 // (kMerge false: no word of the tile lies before split.)
-template <int NT, bool kMerge>
+// With `pre` the tile's sign|mantissa bytes are sm_pre (loaded earlier for
+// the whole tile).
+template <int NT, bool kX1, bool kMerge>
 __device__ __forceinline__ void tile_step(uint32_t tt, uint32_t w_lo, uint32_t w_hi, uint32_t split,
                                           uint32_t t_base, const uint8_t *tile,
-                                          const uint8_t *signmant, const XSrc &xs, uint32_t seg_tile,
-                                          uint32_t lane, uint2 carry, f32x4 (&acc)[NT]) {
+                                          const uint8_t *signmant, XSrc &xs, uint32_t seg_tile,
+                                          uint32_t lane, uint2 carry, bool pre, uint2 sm_pre,
+                                          f32x4 (&acc)[NT]) {
     u32x4 bv[NT];
-    tile_x<NT>(bv, xs, tt - seg_tile);
+    tile_x<NT, kX1>(bv, xs, tt - seg_tile);
     const uint32_t q = (tt << 9) + 8 * lane;
-    const uint2 sm = q + 8 > w_lo && q < w_hi ? load_sm8(signmant + q) : make_uint2(0, 0);
+    const uint2 sm = pre ? sm_pre
+                         : (q + 8 > w_lo && q < w_hi ? load_sm8(signmant + q) : make_uint2(0, 0));
     uint2 e;
     if (kMerge)
         e = tile_exps(tile, t_base, q, split, w_hi, carry);
@@ -1297,17 +1325,22 @@ __device__ __forceinline__ void tile_step(uint32_t tt, uint32_t w_lo, uint32_t w
 }
 
 // An operand tile wholly inside the block's decoded words: no masks.
-template <int NT>
+template <int NT, bool kX1>
 __device__ __forceinline__ void tile_whole(uint32_t tt, uint32_t t_base, const uint8_t *tile,
-                                           const uint8_t *signmant, const XSrc &xs, uint32_t seg_tile,
-                                           uint32_t lane, f32x4 (&acc)[NT]) {
+                                           const uint8_t *signmant, XSrc &xs, uint32_t seg_tile,
+                                           uint32_t lane, bool pre, uint2 sm_pre, f32x4 (&acc)[NT]) {
     u32x4 bv[NT];
-    tile_x<NT>(bv, xs, tt - seg_tile);
+    tile_x<NT, kX1>(bv, xs, tt - seg_tile);
     const uint32_t q = (tt << 9) + 8 * lane;
     const uint4 w = join8(*reinterpret_cast<const uint2 *>(tile + (q - t_base)),
-                          load_sm8(signmant + q));
+                          pre ? sm_pre : load_sm8(signmant + q));
     tile_mfma<NT>(acc, u32x4{w.x, w.y, w.z, w.w}, bv);
 }
+
+// Sign|mantissa bytes of a window's first operand tiles, loaded at the top
+// of the block so that they arrive while it decodes.
+// (Two with one vector: a third takes that kernel past its 64 VGPRs.)
+template <bool kX1> constexpr int kSmAhead = kX1 ? 2 : 3;
 
 // Multiply the operand tiles that words [w_lo, w_hi) reach into acc.  Words
 // [w_lo, split) were decoded by the wave's earlier blocks and sit in carry
@@ -1315,24 +1348,38 @@ __device__ __forceinline__ void tile_whole(uint32_t tt, uint32_t t_base, const u
 // LDS tile (word q at byte q - t_base).  With `defer` the last tile, which
 // the wave's next block completes, is not multiplied: its exponent bytes go
 // to carry instead.
-template <int NT>
+// With `pre`, smp[k] holds the sign|mantissa bytes of tile (w_lo >> 9) + k.
+template <int NT, bool kX1>
 __device__ __forceinline__ void mfma_window(uint32_t w_lo, uint32_t split, uint32_t w_hi,
                                             bool defer, uint32_t t_base, const uint8_t *tile,
-                                            const uint8_t *signmant, const XSrc &xs,
+                                            const uint8_t *signmant, XSrc &xs,
                                             uint32_t seg_tile, uint32_t lane, uint2 &carry,
+                                            bool pre, const uint2 (&smp)[kSmAhead<kX1>],
                                             f32x4 (&acc)[NT]) {
     uint32_t tt = w_lo >> 9;
     const uint32_t t_end = defer ? w_hi >> 9 : (w_hi + 511) >> 9;
+    const uint32_t t_whole = w_hi >> 9;  // tiles below it end inside the window
     if (tt < t_end) {  // the first tile: carried words merged
-        tile_step<NT, true>(tt, w_lo, w_hi, split, t_base, tile, signmant, xs, seg_tile, lane, carry,
-                            acc);
+        tile_step<NT, kX1, true>(tt, w_lo, w_hi, split, t_base, tile, signmant, xs, seg_tile, lane, carry,
+                            pre, smp[0], acc);
+        ++tt;
         // the block's later tiles (split lies below them): whole ones, then a
-        // last partial one
-        for (++tt; tt < (w_hi >> 9); ++tt)
-            tile_whole<NT>(tt, t_base, tile, signmant, xs, seg_tile, lane, acc);
+        // last partial one; the first of them with the bytes loaded ahead
+#pragma unroll
+        for (int k = 1; k < kSmAhead<kX1>; ++k) {
+            if (tt >= t_end) break;
+            if (tt < t_whole)
+                tile_whole<NT, kX1>(tt, t_base, tile, signmant, xs, seg_tile, lane, pre, smp[k], acc);
+            else
+                tile_step<NT, kX1, false>(tt, w_lo, w_hi, split, t_base, tile, signmant, xs, seg_tile,
+                                     lane, carry, pre, smp[k], acc);
+            ++tt;
+        }
+        for (; tt < t_whole; ++tt)
+            tile_whole<NT, kX1>(tt, t_base, tile, signmant, xs, seg_tile, lane, false, smp[0], acc);
         if (tt < t_end) {
-            tile_step<NT, false>(tt, w_lo, w_hi, split, t_base, tile, signmant, xs, seg_tile, lane,
-                                 carry, acc);
+            tile_step<NT, kX1, false>(tt, w_lo, w_hi, split, t_base, tile, signmant, xs, seg_tile, lane,
+                                 carry, false, smp[0], acc);
             ++tt;
         }
     }
@@ -1341,13 +1388,13 @@ __device__ __forceinline__ void mfma_window(uint32_t w_lo, uint32_t split, uint3
 
 // The carried words [c_lo, c_hi) alone (the wave's next block does not go on
 // with them).
-template <int NT>
+template <int NT, bool kX1>
 __device__ __forceinline__ void flush_carry(uint32_t c_lo, uint32_t c_hi, const uint8_t *signmant,
-                                            const XSrc &xs, uint32_t seg_tile, uint32_t lane,
+                                            XSrc &xs, uint32_t seg_tile, uint32_t lane,
                                             uint2 carry, f32x4 (&acc)[NT]) {
     // split past the window: every exponent byte from carry, no LDS read
-    tile_step<NT, true>(c_lo >> 9, c_lo, c_hi, 0xFFFFFFFFu, 0u, nullptr, signmant, xs, seg_tile,
-                        lane, carry, acc);
+    tile_step<NT, kX1, true>(c_lo >> 9, c_lo, c_hi, 0xFFFFFFFFu, 0u, nullptr, signmant, xs, seg_tile,
+                        lane, carry, false, carry, acc);
 }
 
 // Input ranges for df11_tile_inputs_kernel: range r is x[b * x_stride +
@@ -1391,10 +1438,12 @@ template <int NT> struct TiledOccupancy {
     static constexpr int kValue = NT == 1 ? 8 : NT == 2 ? kWavesPerEu : 4;
 };
 
-template <int NT>
+// kX1: one vector (NT 1, row-major x).
+template <int NT, bool kX1>
 __global__ __launch_bounds__(kGroupThreads)
 __attribute__((amdgpu_waves_per_eu(TiledOccupancy<NT>::kValue)))
 void df11_tiled_kernel(DecodeArgs a, TiledArgs t) {
+    static_assert(!kX1 || NT == 1, "the one-vector inputs are for one group of vectors");
     __shared__ __attribute__((aligned(16))) uint8_t lds_static[kStaticLds];
     static_assert(8 * 4 * 256 * 4 <= kStaticLds, "the final sums of 8 waves fit the static LDS");
     extern __shared__ uint4 smem_u4[];
@@ -1447,6 +1496,10 @@ void df11_tiled_kernel(DecodeArgs a, TiledArgs t) {
     xs.live = 0;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) xs.live |= (16 * nt + lane % 16 < t.batch ? 1u : 0u) << nt;
+    xs.ks0 = 0xFFFFFFF0u;  // none held
+    xs.xw = 0;
+    xs.cols = 32 * ks_e;
+    if (kX1) xs.xl = (const g_cu16 *)t.x + xoff_e;  // vector 0's inputs of the matrix
 
     // tables into LDS while the wave's first block loads
     const uint32_t hier_bytes = a.n_tables * kTableBytes;
@@ -1480,8 +1533,13 @@ void df11_tiled_kernel(DecodeArgs a, TiledArgs t) {
     uint2 carry = make_uint2(0, 0);
     uint32_t c_lo = 0, c_hi = 0;
     for (; b < r_hi; ++b) {
+        // Every load of the last block is done by now (this block's inputs were
+        // issued a block ago).  Saying so here leaves the compiler no load in
+        // flight to guard across the loop: otherwise a register reused in
+        // phase 1 can draw a wait for everything, this block's prefetches
+        // included.
+        __builtin_amdgcn_s_waitcnt(0);
         const BlockIn cur = nxt;
-        if (b + 1 < r_hi) nxt = load_block(a, b + 1, lane);
         const uint32_t p0 = __builtin_amdgcn_readlane(cur.pos, 0);
         const uint32_t p1 = __builtin_amdgcn_readlane(cur.pos, 1);
         const bool sane = p1 >= p0 && p1 <= a.n && p1 - p0 <= (uint32_t)kMaxBlockCodes;
@@ -1490,6 +1548,32 @@ void df11_tiled_kernel(DecodeArgs a, TiledArgs t) {
         const bool one_pass = groups * 8 + 4 <= (uint32_t)kTileCap;
         // the block's words in this segment
         const uint32_t w_lo = p0 > seg_lo ? p0 : seg_lo, w_hi = p1 < seg_hi ? p1 : seg_hi;
+        // the carried words go on at w_lo (a run's blocks are consecutive)
+        const bool go_on = c_lo < c_hi && c_hi == w_lo && w_lo < w_hi;
+        // Loads for this block and the next, oldest first: loads complete in
+        // order, so the tiles' first wait (for the inputs) must not sit behind
+        // the next block's stream words.  One vector: the inputs of the
+        // window's first 4 k-steps (a column past the matrix repeats its last
+        // pair).  Then the next block, then the sign|mantissa bytes of the
+        // window's first tiles (a tile past the window's last one repeats
+        // that one).
+        const bool pre = one_pass && w_lo < w_hi;
+        if (kX1 && pre) {
+            xs.ks0 = ((go_on ? c_lo : w_lo) >> 9) - seg_tile;
+            uint32_t col = 32 * xs.ks0 + 2 * lane;
+            col = col < xs.cols - 2 ? col : xs.cols - 2;
+            xs.xw = *(const __attribute__((address_space(1))) uint32_t *)(xs.xl + col);
+        }
+        if (b + 1 < r_hi) nxt = load_block(a, b + 1, lane);
+        uint2 smp[kSmAhead<kX1>];
+        {
+            const uint32_t t0 = (go_on ? c_lo : w_lo) >> 9, t_last = pre ? (w_hi - 1) >> 9 : t0;
+#pragma unroll
+            for (int k = 0; k < kSmAhead<kX1>; ++k) {
+                const uint32_t t = t0 + k < t_last ? t0 + k : t_last;
+                smp[k] = pre ? load_sm8(a.signmant + (t << 9) + 8 * lane) : make_uint2(0, 0);
+            }
+        }
         const uint32_t gw = __builtin_amdgcn_alignbit(cur.g1, cur.g0, gap_shift);
         const uint32_t gap = gw & 31u, gap_next = (gw >> 5) & 31u;
         // stop bit and stream end relative to this lane's slice (as in the decode)
@@ -1525,7 +1609,7 @@ void df11_tiled_kernel(DecodeArgs a, TiledArgs t) {
         const uint32_t total = __builtin_amdgcn_readlane(incl, kWave - 1);
         if (!sane || total != p1 - p0) {  // a corrupt block: reported, its words left out
             if (lane == 0 && a.status) atomicAdd(a.status, 1u);
-            if (c_lo < c_hi) flush_carry<NT>(c_lo, c_hi, a.signmant, xs, seg_tile, lane, carry, acc);
+            if (c_lo < c_hi) flush_carry<NT, kX1>(c_lo, c_hi, a.signmant, xs, seg_tile, lane, carry, acc);
             c_hi = c_lo;
             wave_lds_sync();
             continue;
@@ -1550,17 +1634,15 @@ void df11_tiled_kernel(DecodeArgs a, TiledArgs t) {
                          tile_addr + at);
             wave_lds_sync();
         }
-        // the carried words go on at w_lo (a run's blocks are consecutive)
-        const bool go_on = c_lo < c_hi && c_hi == w_lo && w_lo < w_hi;
         if (c_lo < c_hi && !(go_on && one_pass))
-            flush_carry<NT>(c_lo, c_hi, a.signmant, xs, seg_tile, lane, carry, acc);
+            flush_carry<NT, kX1>(c_lo, c_hi, a.signmant, xs, seg_tile, lane, carry, acc);
         if (one_pass) {
             if (w_lo < w_hi) {
                 // leave the last tile to the next block if that block completes it
                 const bool defer = b + 1 < r_hi && (w_hi & 511u) != 0;
                 const uint32_t lo = go_on ? c_lo : w_lo;
-                mfma_window<NT>(lo, w_lo, w_hi, defer, base, tile, a.signmant, xs, seg_tile, lane,
-                                carry, acc);
+                mfma_window<NT, kX1>(lo, w_lo, w_hi, defer, base, tile, a.signmant, xs, seg_tile, lane,
+                                carry, pre, smp, acc);
                 c_lo = defer ? (lo > ((w_hi - 1) & ~511u) ? lo : (w_hi - 1) & ~511u) : 0u;
                 c_hi = defer ? w_hi : 0u;
             } else {
@@ -1577,8 +1659,8 @@ void df11_tiled_kernel(DecodeArgs a, TiledArgs t) {
                 const uint32_t r_lo = base + r0, r_hi = base + r0 + kTileCap;
                 const uint32_t v_lo = w_lo > r_lo ? w_lo : r_lo, v_hi = w_hi < r_hi ? w_hi : r_hi;
                 if (v_lo < v_hi)
-                    mfma_window<NT>(v_lo, v_lo, v_hi, false, r_lo, tile, a.signmant, xs, seg_tile,
-                                    lane, carry, acc);
+                    mfma_window<NT, kX1>(v_lo, v_lo, v_hi, false, r_lo, tile, a.signmant, xs, seg_tile,
+                                    lane, carry, false, smp, acc);
                 wave_lds_sync();
             }
         }
@@ -1984,8 +2066,10 @@ extern "C" int df11_decode_gemm_tiled(const df11_device_stream *s, const df11_ge
     t.first[n_mats] = run;
     const dim3 grid(run), block(kGroupThreads);
     const size_t lds = lds_bytes(s->n_tables);
-    if (groups == 1) hipLaunchKernelGGL(df11_tiled_kernel<1>, grid, block, lds, hs, a, t);
-    else if (groups == 2) hipLaunchKernelGGL(df11_tiled_kernel<2>, grid, block, lds, hs, a, t);
-    else hipLaunchKernelGGL(df11_tiled_kernel<4>, grid, block, lds, hs, a, t);
+    if (groups == 1 && batch == 1 && !t.xt)
+        hipLaunchKernelGGL((df11_tiled_kernel<1, true>), grid, block, lds, hs, a, t);
+    else if (groups == 1) hipLaunchKernelGGL((df11_tiled_kernel<1, false>), grid, block, lds, hs, a, t);
+    else if (groups == 2) hipLaunchKernelGGL((df11_tiled_kernel<2, false>), grid, block, lds, hs, a, t);
+    else hipLaunchKernelGGL((df11_tiled_kernel<4, false>), grid, block, lds, hs, a, t);
     return hipGetLastError() == hipSuccess ? DF11_OK : DF11_ERR_HIP;
 }

@@ -175,7 +175,7 @@ def test_tiled_exact_flat_codes(torch):
     w = wl.random_small(n, 9, "uniform")
     e = ((w >> 7) & 0xFF) % 3 + (127 - 8)
     w = (w & 0x807F) | (e.astype(np.uint16) << 7)
-    for batch in (3, 64):
+    for batch in (1, 3, 64):
         _check(torch, w, shapes, batch, "exact_flat", exact=True)
 
 
@@ -201,10 +201,12 @@ def test_tiled_llama8b_block_full(torch):
            exact=False)
 
 
-def test_tiled_corrupt_blocks_stay_contained(torch):
+@pytest.mark.parametrize("batch", [1, 8])
+def test_tiled_corrupt_blocks_stay_contained(torch, batch):
     """Flipped stream bits: the blocks whose counts no longer match are
     counted in the status word and left out; nothing is written outside y,
-    and every segment whose blocks are all intact is still exact."""
+    and every segment whose blocks are all intact is still exact (one vector
+    runs its own kernel, with the inputs gathered across the wave)."""
     import dataclasses
     shapes = [(64, 4096), (32, 8192)]
     w = _exact_weights(sum(r * c for r, c in shapes), 61)
@@ -219,7 +221,6 @@ def test_tiled_corrupt_blocks_stay_contained(torch):
             stream[bit >> 3] ^= np.uint8(1 << (bit & 7))
             hit |= {b, b - 1}
     bad = hd.TiledEncoded(dataclasses.replace(te.enc, stream=stream), te.mats, te.seg_blk)
-    batch = 8
     nx = max(m.x_offset + m.cols for m in te.mats)
     x_bits = np.array([0xBF80, 0, 0x3F80], np.uint16)[rng.integers(0, 3, (batch, nx))]
     st = torch.zeros(1, dtype=torch.int32, device="cuda")
