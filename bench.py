@@ -175,11 +175,13 @@ def run_copy(args) -> int:
     return 0
 
 
-def launch_time_ms(launch, stream, reps=20, warmup=100) -> float:
+def launch_time_ms(launch, stream, reps=20, warmup=300) -> float:
     """Average duration of launch(k) over `reps` back-to-back calls between one
-    pair of events on `stream`, after `warmup` untimed calls (the GPU's clocks
-    take about a hundred back-to-back launches to ramp up after an idle
-    stretch, such as a host-side encode)."""
+    pair of events on `stream`, after `warmup` untimed calls (after an idle
+    stretch, such as a host-side encode, the GPU's clocks take over a hundred
+    back-to-back launches of ~0.1 ms to settle: a kernel trace of the tiled
+    product showed launches 20-50 at 129 us and launch 110 still falling, at
+    111 us)."""
     import torch
     for k in range(warmup):
         launch(k)
@@ -424,7 +426,7 @@ def fused_gemm(wlx, copies, stream, batch, reps=20) -> dict:
     return {"fused_ms": round(ms, 5)}
 
 
-def fused_tiled(wlx, stream, batches, n_copies=3, reps=20, warmup=100) -> dict:
+def fused_tiled(wlx, stream, batches, n_copies=3, reps=20, warmup=300) -> dict:
     """y_b = W x_b for `batch` vectors on the matrix cores from the block
     encoded in operand-tile order (df11_decode_gemm_tiled), timed over
     back-to-back launches on rotating copies like the decode."""
