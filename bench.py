@@ -728,7 +728,7 @@ def main() -> int:
             fused[f"batch{b}"] = f
         line["decode_vs_gemm"]["fused"] = fused
         # the tiled product on the matrix cores (its own tile-order encoding)
-        tiled = fused_tiled(wlx, stream, (1, 16, 64))
+        tiled = fused_tiled(wlx, stream, (1, 2, 4, 16, 64))
         for key, f in tiled.items():
             g = line["decode_vs_gemm"][key]["gemm_ms"]
             f["over_bf16_gemm"] = round(f["fused_ms"] / g, 4)
