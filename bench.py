@@ -263,8 +263,8 @@ def run_stack(args) -> int:
     the time of one forward pass (all blocks) for the decodes alone, the GEMMs
     alone on resident BF16 weights, decode+GEMMs on one stream, decode of
     block i+1 overlapped with the GEMMs of block i on two streams, and the
-    fused products; and their ratios.  Single-stream schedules run as
-    captured HIP graphs."""
+    fused products; and their ratios.  Every schedule runs as a captured HIP
+    graph."""
     import numpy as np
     import torch
     import huffman_decode_amd as hd
@@ -306,10 +306,10 @@ def run_stack(args) -> int:
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / reps
 
-    # Single-stream schedules are replayed as HIP graphs (hundreds of small
-    # launches per forward pass would otherwise partly time the host); each
-    # graph's replays are checked against the eager outputs first.  The
-    # two-stream overlapped schedule runs eagerly.
+    # Every schedule is replayed as a HIP graph (hundreds of small launches
+    # per forward pass would otherwise partly time the host); the overlapped
+    # one forks to the decode stream and joins back inside its graph.  Each
+    # graph's replays are checked against the eager outputs first.
     def graphed(fn, outputs):
         g = captured(fn, outputs)
         return lambda: g.replay(), g
@@ -325,8 +325,11 @@ def run_stack(args) -> int:
         run, g3 = graphed(lambda: runner.run_serial(acts, outs), outs_list)
         t_ser = timed(run, args.steps)
         del g1, g2, g3
-        t_ovl = {g: timed(lambda: runner.run_overlapped(acts, outs, g), args.steps)
-                 for g in (0, 512, 384, 256)}
+        t_ovl = {}
+        for cap in (0, 512, 384, 256):
+            run, g6 = graphed(lambda cap=cap: runner.run_overlapped(acts, outs, cap), outs_list)
+            t_ovl[cap] = timed(run, args.steps)
+            del g6
         best = min(t_ovl, key=t_ovl.get)
         # the fused product in place of decode-then-GEMM (small batches only)
         t_fused = None
