@@ -1432,8 +1432,9 @@ __global__ __launch_bounds__(256) void df11_tile_inputs_kernel(TileInputs t) {
     *(__attribute__((address_space(1))) u32x4 *)((__attribute__((address_space(1))) uint16_t *)t.xt + at) = v;
 }
 
-// Occupancy: up to 32 vectors the decode's 80-VGPR budget (3 workgroups per
-// CU); 64 vectors 128 VGPRs (2 per CU).
+// Occupancy: up to 16 vectors 8 waves per SIMD (64 VGPRs, ~80 SGPRs: 4
+// workgroups per CU); up to 32 the decode's 80-VGPR budget (3 per CU); 64
+// vectors 128 VGPRs (2 per CU).
 template <int NT> struct TiledOccupancy {
     static constexpr int kValue = NT == 1 ? 8 : NT == 2 ? kWavesPerEu : 4;
 };
@@ -1940,8 +1941,10 @@ extern "C" int df11_decode_gemm_noalloc(const df11_device_stream *s, const df11_
 // Batches from this size on read their inputs rewritten k-step-major: a wave's
 // 16 B loads of one k-step then cover 1 KB in one piece instead of 64 bytes
 // of each of 16 rows, which the memory pipeline serves far faster (batch 64:
-// 0.34 -> 0.23 ms on the 8B-shaped block).  Smaller batches read x directly.
-constexpr uint32_t kTiledRewriteBatch = 8;
+// 0.34 -> 0.23 ms on the 8B-shaped block), at the cost of a ~5 us kernel.
+// Smaller batches read x directly: at 8 vectors that is 2% faster, at 12 the
+// two tie, at 16 the rewrite is 4% faster.
+constexpr uint32_t kTiledRewriteBatch = 12;
 
 static uint32_t tiled_groups(uint32_t batch) { return batch <= 16 ? 1u : batch <= 32 ? 2u : 4u; }
 

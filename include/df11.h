@@ -287,7 +287,7 @@ int df11_tile_segments(const uint32_t *block_pos, uint32_t n_blocks, const df11_
 #define DF11_TILED_MAX_BATCH 64
 
 /* Bytes of device workspace df11_decode_gemm_tiled needs for this matrix list
- * and batch: 0 below 8 vectors; from 8 on, room for the inputs rewritten
+ * and batch: 0 below 12 vectors; from 12 on, room for the inputs rewritten
  * k-step-major (2 bytes x 16 vectors per group of 16 in the batch x the
  * columns of the distinct input ranges (x_offset, cols)).  0 also for a bad
  * list or batch. */
@@ -307,7 +307,7 @@ uint64_t df11_tiled_workspace_bytes(const df11_gemv_matrix *mats, uint32_t n_mat
  * multiple of 8 for x, below 2^32, at least every matrix's end; ignored for
  * batch 1).  workspace: caller-owned device memory of at least
  * df11_tiled_workspace_bytes (16-byte aligned; may be null when that is 0),
- * overwritten: from 8 vectors on, a first kernel copies the inputs there
+ * overwritten: from 12 vectors on, a first kernel copies the inputs there
  * k-step-major ([k-step][vector][32 columns]), so that each wave's loads of
  * one k-step read one contiguous kilobyte.  One or two kernels enqueued on
  * hip_stream.  A block whose decoded count disagrees with block_pos is

@@ -135,7 +135,7 @@ def test_tiled_exact_batches(torch, batch):
     _check(torch, w, shapes, batch, "exact_mixed", exact=True)
 
 
-@pytest.mark.parametrize("batch", [8, 64])
+@pytest.mark.parametrize("batch", [8, 12, 64])
 def test_tiled_exact_shared_inputs(torch, batch):
     """Matrices that read the same input range: the inputs are rewritten once
     for all of them."""

@@ -432,15 +432,15 @@ def test_tile_segments_match_a_search_of_block_pos():
 
 def test_tiled_workspace_size_and_refusal():
     """The tiled product's workspace holds the inputs rewritten k-step-major
-    from 8 vectors on: 2 bytes x 16 per group of 16 vectors x the columns of
+    from 12 vectors on: 2 bytes x 16 per group of 16 vectors x the columns of
     the distinct input ranges; a shorter workspace is refused before any
     device call."""
     lib = hd.library()
     shapes = [(64, 4096), (32, 2048)]
     mats, _, _ = hd.gemv_matrices(shapes)
     assert hd.df11_tiled_workspace_bytes(mats, 1) == 0
-    assert hd.df11_tiled_workspace_bytes(mats, 7) == 0
-    assert hd.df11_tiled_workspace_bytes(mats, 8) == 2 * 16 * (4096 + 2048)
+    assert hd.df11_tiled_workspace_bytes(mats, 11) == 0
+    assert hd.df11_tiled_workspace_bytes(mats, 12) == 2 * 16 * (4096 + 2048)
     assert hd.df11_tiled_workspace_bytes(mats, 33) == 2 * 64 * (4096 + 2048)
     assert hd.df11_tiled_workspace_bytes(mats, 65) == 0
     shared = [hd.GemvMatrix(0, 64, 4096, 0, 0), hd.GemvMatrix(64 * 4096, 32, 4096, 0, 64)]
