@@ -195,9 +195,12 @@ def test_tiled_flux_and_70b_down(torch):
     _check(torch, w, shapes, 64, "70b_down_rows", exact=False)
 
 
-def test_tiled_llama8b_block_full(torch):
+@pytest.mark.parametrize("batch", [1, 64])
+def test_tiled_llama8b_block_full(torch, batch):
+    """The full 8B-shaped block at the batches the benchmark times first and
+    last (1: the one-vector kernel; 64: four groups of 16)."""
     wlx = wl.llama8b_block()
-    _check(torch, wlx.weights, [(m.rows, m.cols) for m in wlx.matrices], 64, "llama8b_block",
+    _check(torch, wlx.weights, [(m.rows, m.cols) for m in wlx.matrices], batch, "llama8b_block",
            exact=False)
 
 
