@@ -180,6 +180,58 @@ def run_copy(args) -> int:
     return 0
 
 
+def run_stream(args) -> int:
+    """The GPU's own streaming rates, beside which the decode's figure is read:
+    read-only, write-only and copy kernels of the library (16-byte accesses,
+    four in flight per thread) over --copy-mib MiB, and torch's fill and copy,
+    on rotating buffers that span at least 768 MB."""
+    import torch
+    import huffman_decode_amd as hd
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    nbytes = args.copy_mib << 20
+    k_bufs = max(3, -(-768_000_000 // nbytes))
+    src = [torch.empty(nbytes // 4, dtype=torch.int32, device=dev).random_(-1000, 1000)
+           for _ in range(k_bufs)]
+    dst = [torch.empty_like(t) for t in src]
+    grids = (2048, 8192, 32768)  # workgroups of 256 threads; reads favour few, writes many
+    slots = torch.empty(max(hd.df11_stream_read_slots(nbytes, g) for g in grids),
+                        dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    legs = {
+        "read_only": (nbytes, lambda k, g: hd.df11_stream_read(src[k % k_bufs], slots, nbytes, g,
+                                                                 stream)),
+        "write_only": (nbytes, lambda k, g: hd.df11_stream_write(dst[k % k_bufs], nbytes, k, g,
+                                                                   stream)),
+        "copy": (2 * nbytes, lambda k, g: hd.df11_stream_copy(src[k % k_bufs], dst[k % k_bufs],
+                                                              nbytes, g, stream)),
+    }
+    res = {"mode": "stream", "bytes_each_way": nbytes, "rotating_buffers": k_bufs}
+    for name, (moved, fn) in legs.items():
+        best = None
+        for g in grids:  # the best grid of the three
+            ms = launch_time_ms(lambda k: fn(k, g), stream, reps=args.steps, warmup=args.warmup)
+            if best is None or ms < best[0]:
+                best = (ms, g)
+        res[name] = {"kernel_ms": round(best[0], 5), "grid": best[1],
+                     "GBps": round(moved / (best[0] * 1e-3) / 1e9, 1)}
+    for name, (moved, fn) in {"torch_fill": (nbytes, lambda k: dst[k % k_bufs].fill_(k)),
+                              "torch_copy": (2 * nbytes,
+                                             lambda k: dst[k % k_bufs].copy_(src[k % k_bufs]))}.items():
+        ms = launch_time_ms(fn, stream, reps=args.steps, warmup=args.warmup)
+        res[name] = {"kernel_ms": round(ms, 5), "GBps": round(moved / (ms * 1e-3) / 1e9, 1)}
+    # the kernels did what they say
+    hd.df11_stream_copy(src[0], dst[0], nbytes, stream=stream)
+    hd.df11_stream_read(src[0], slots, nbytes, stream=stream)
+    torch.cuda.synchronize()
+    import numpy as np
+    want = int(np.bitwise_xor.reduce(src[0].cpu().numpy()))
+    got = int(np.bitwise_xor.reduce(slots.cpu().numpy()))
+    res["ok"] = bool(torch.equal(src[0], dst[0])) and got == want
+    print(json.dumps(res), flush=True)
+    return 0 if res["ok"] else 1
+
+
 def launch_time_ms(launch, stream, reps=20, warmup=300) -> float:
     """Average duration of launch(k) over `reps` back-to-back calls between one
     pair of events on `stream`, after `warmup` untimed calls (after an idle
@@ -561,9 +613,11 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-gemm", action="store_true", help="skip the decode/GEMM ratios")
     ap.add_argument("--mode", choices=("decode", "copy", "stack", "encode", "offload", "ceiling",
-                                       "tiled"),
+                                       "tiled", "stream"),
                     default="decode",
                     help="ceiling: only the traffic-only kernel on the workload's bytes; "
+                         "stream: the GPU's read-only, write-only and copy rates over "
+                         "--copy-mib MiB; "
                          "tiled: only the tiled product at --batches; "
                          "copy: time a plain device copy of --copy-mib MiB instead; "
                          "stack: decode/GEMM schedules over the 32-block 8B-shaped stack; "
@@ -573,7 +627,7 @@ def main() -> int:
     ap.add_argument("--batches", default="1,16,64", help="vectors per call in the tiled mode")
     ap.add_argument("--copy-mib", type=int, default=1024)
     args = ap.parse_args()
-    fast = args.mode in ("decode", "copy", "ceiling")
+    fast = args.mode in ("decode", "copy", "ceiling", "stream")
     if args.steps is None:
         args.steps = 100 if fast else 20
     if args.warmup is None:
@@ -595,6 +649,8 @@ def main() -> int:
         return run_offload(args)
     if args.mode == "tiled":
         return run_tiled(args)
+    if args.mode == "stream":
+        return run_stream(args)
 
     import numpy as np
     import torch

@@ -124,6 +124,14 @@ def _load():
         lib.df11_tiled_workspace_bytes.restype = _U64
         lib.df11_stream_ceiling.argtypes = [_P, _P, _U64, _P, _U64, _U32, _P]
         lib.df11_stream_ceiling.restype = ctypes.c_int
+        lib.df11_stream_read_slots.argtypes = [_U64, _U32]
+        lib.df11_stream_read_slots.restype = _U32
+        lib.df11_stream_read.argtypes = [_P, _U64, _P, _U64, _U32, _P]
+        lib.df11_stream_read.restype = ctypes.c_int
+        lib.df11_stream_write.argtypes = [_P, _U64, _U32, _U32, _P]
+        lib.df11_stream_write.restype = ctypes.c_int
+        lib.df11_stream_copy.argtypes = [_P, _P, _U64, _U32, _P]
+        lib.df11_stream_copy.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -535,3 +543,48 @@ def df11_stream_ceiling(a, b, out, n: int, max_groups: int = 0, stream=None) -> 
     _check("df11_stream_ceiling", _load().df11_stream_ceiling(
         a.data_ptr(), 0 if b is None else b.data_ptr(), b_bytes, out.data_ptr(), n, max_groups,
         stream.cuda_stream))
+
+
+def _nbytes(t) -> int:
+    return t.numel() * t.element_size()
+
+
+def df11_stream_read_slots(nbytes: int, grid: int = 0) -> int:
+    return int(_load().df11_stream_read_slots(nbytes, grid))
+
+
+def df11_stream_read(src, out, nbytes: int, grid: int = 0, stream=None) -> None:
+    """Enqueue the read-only stream over src[0..nbytes) (CUDA tensors; out an
+    int32/uint32 tensor of at least df11_stream_read_slots(nbytes, grid)
+    elements, receiving one XOR of 32-bit words per thread)."""
+    import torch
+    if _nbytes(src) < nbytes:
+        raise ValueError("src is smaller than nbytes")
+    if out.element_size() != 4:
+        raise ValueError("out must hold 32-bit words")
+    if stream is None:
+        stream = torch.cuda.current_stream(src.device)
+    _check("df11_stream_read", _load().df11_stream_read(
+        src.data_ptr(), nbytes, out.data_ptr(), out.numel(), grid, stream.cuda_stream))
+
+
+def df11_stream_write(dst, nbytes: int, value: int = 0, grid: int = 0, stream=None) -> None:
+    """Enqueue the write-only stream over dst[0..nbytes) (a CUDA tensor)."""
+    import torch
+    if _nbytes(dst) < nbytes:
+        raise ValueError("dst is smaller than nbytes")
+    if stream is None:
+        stream = torch.cuda.current_stream(dst.device)
+    _check("df11_stream_write", _load().df11_stream_write(
+        dst.data_ptr(), nbytes, value & 0xFFFFFFFF, grid, stream.cuda_stream))
+
+
+def df11_stream_copy(src, dst, nbytes: int, grid: int = 0, stream=None) -> None:
+    """Enqueue dst[0..nbytes) = src[0..nbytes) (CUDA tensors)."""
+    import torch
+    if _nbytes(src) < nbytes or _nbytes(dst) < nbytes:
+        raise ValueError("src or dst is smaller than nbytes")
+    if stream is None:
+        stream = torch.cuda.current_stream(dst.device)
+    _check("df11_stream_copy", _load().df11_stream_copy(
+        src.data_ptr(), dst.data_ptr(), nbytes, grid, stream.cuda_stream))

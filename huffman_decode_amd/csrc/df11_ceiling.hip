@@ -89,3 +89,134 @@ extern "C" int df11_stream_ceiling(const uint8_t *a, const uint8_t *b, uint64_t 
                        static_cast<hipStream_t>(hip_stream), a, b, b_bytes / 16, out, groups);
     return hipGetLastError() == hipSuccess ? DF11_OK : DF11_ERR_HIP;
 }
+
+// ---------------------------------------------------------------- plain streams
+//
+// Read-only, write-only and copy kernels over `bytes` (a multiple of 16) with
+// 16-byte accesses: the GPU's own streaming limits, beside which the decode's
+// figure and its same-pattern ceiling above are read.  A thread keeps four
+// accesses in flight (at a stride of the workgroup size: each access of a
+// wave covers 1 KB in one piece, which was faster than 64 contiguous bytes
+// per thread).  The default grid, 128 workgroups of 256 threads per compute
+// unit, was the fastest tried for writes and copies (1 or 4 deep, 2048 to
+// 32768 workgroups); reads run faster on fewer (2048).
+
+namespace {
+
+constexpr int kStreamThreads = 256;
+constexpr int kStreamDepth = 4;
+constexpr int kStreamGroupsPerCu = 128;
+
+__global__ __launch_bounds__(kStreamThreads) void df11_stream_read_kernel(const u32x4 *src,
+                                                                          uint64_t n16,
+                                                                          uint32_t *out) {
+    const uint64_t t = (uint64_t)blockIdx.x * kStreamThreads + threadIdx.x;
+    const uint64_t stride = (uint64_t)gridDim.x * kStreamThreads * kStreamDepth;
+    u32x4 acc = {0, 0, 0, 0};
+    for (uint64_t i = (uint64_t)blockIdx.x * kStreamThreads * kStreamDepth + threadIdx.x; i < n16;
+         i += stride) {
+        u32x4 r[kStreamDepth];
+#pragma unroll
+        for (int d = 0; d < kStreamDepth; ++d) {
+            const uint64_t j = i + (uint64_t)d * kStreamThreads;
+            r[d] = j < n16 ? src[j] : u32x4{0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int d = 0; d < kStreamDepth; ++d) acc ^= r[d];
+    }
+    out[t] = acc.x ^ acc.y ^ acc.z ^ acc.w;
+}
+
+__global__ __launch_bounds__(kStreamThreads) void df11_stream_write_kernel(u32x4 *dst, uint64_t n16,
+                                                                           uint32_t value) {
+    const uint64_t stride = (uint64_t)gridDim.x * kStreamThreads * kStreamDepth;
+    for (uint64_t i = (uint64_t)blockIdx.x * kStreamThreads * kStreamDepth + threadIdx.x; i < n16;
+         i += stride) {
+#pragma unroll
+        for (int d = 0; d < kStreamDepth; ++d) {
+            const uint64_t j = i + (uint64_t)d * kStreamThreads;
+            if (j < n16) dst[j] = u32x4{value, value, value, (uint32_t)j};
+        }
+    }
+}
+
+__global__ __launch_bounds__(kStreamThreads) void df11_stream_copy_kernel(const u32x4 *src,
+                                                                          u32x4 *dst,
+                                                                          uint64_t n16) {
+    const uint64_t stride = (uint64_t)gridDim.x * kStreamThreads * kStreamDepth;
+    for (uint64_t i = (uint64_t)blockIdx.x * kStreamThreads * kStreamDepth + threadIdx.x; i < n16;
+         i += stride) {
+        u32x4 r[kStreamDepth];
+#pragma unroll
+        for (int d = 0; d < kStreamDepth; ++d) {
+            const uint64_t j = i + (uint64_t)d * kStreamThreads;
+            r[d] = j < n16 ? src[j] : u32x4{0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int d = 0; d < kStreamDepth; ++d) {
+            const uint64_t j = i + (uint64_t)d * kStreamThreads;
+            if (j < n16) dst[j] = r[d];
+        }
+    }
+}
+
+int stream_grid(uint32_t grid, uint64_t n16, uint32_t *out) {
+    if (grid == 0) {
+        int dev = 0, cus = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            return DF11_ERR_HIP;
+        grid = (uint32_t)cus * kStreamGroupsPerCu;
+    }
+    const uint64_t want = (n16 + (uint64_t)kStreamThreads * kStreamDepth - 1) /
+                          ((uint64_t)kStreamThreads * kStreamDepth);
+    *out = (uint32_t)(want < grid ? want : grid);
+    return DF11_OK;
+}
+
+bool bad16(const void *p) { return !p || reinterpret_cast<uintptr_t>(p) % 16 != 0; }
+
+}  // namespace
+
+extern "C" uint32_t df11_stream_read_slots(uint64_t bytes, uint32_t grid) {
+    uint32_t g = 0;
+    if (bytes == 0 || bytes % 16 != 0 || stream_grid(grid, bytes / 16, &g) != DF11_OK) return 0;
+    return g * kStreamThreads;
+}
+
+extern "C" int df11_stream_read(const void *src, uint64_t bytes, uint32_t *out, uint64_t out_count,
+                                uint32_t grid, void *hip_stream) {
+    if (bad16(src) || !out || bytes == 0 || bytes % 16 != 0) return DF11_ERR_ARG;
+    uint32_t g = 0;
+    const int st = stream_grid(grid, bytes / 16, &g);
+    if (st != DF11_OK) return st;
+    if (out_count < (uint64_t)g * kStreamThreads) return DF11_ERR_BUFSIZE;
+    hipLaunchKernelGGL(df11_stream_read_kernel, dim3(g), dim3(kStreamThreads), 0,
+                       static_cast<hipStream_t>(hip_stream), static_cast<const u32x4 *>(src),
+                       bytes / 16, out);
+    return hipGetLastError() == hipSuccess ? DF11_OK : DF11_ERR_HIP;
+}
+
+extern "C" int df11_stream_write(void *dst, uint64_t bytes, uint32_t value, uint32_t grid,
+                                 void *hip_stream) {
+    if (bad16(dst) || bytes == 0 || bytes % 16 != 0) return DF11_ERR_ARG;
+    uint32_t g = 0;
+    const int st = stream_grid(grid, bytes / 16, &g);
+    if (st != DF11_OK) return st;
+    hipLaunchKernelGGL(df11_stream_write_kernel, dim3(g), dim3(kStreamThreads), 0,
+                       static_cast<hipStream_t>(hip_stream), static_cast<u32x4 *>(dst), bytes / 16,
+                       value);
+    return hipGetLastError() == hipSuccess ? DF11_OK : DF11_ERR_HIP;
+}
+
+extern "C" int df11_stream_copy(const void *src, void *dst, uint64_t bytes, uint32_t grid,
+                                void *hip_stream) {
+    if (bad16(src) || bad16(dst) || bytes == 0 || bytes % 16 != 0) return DF11_ERR_ARG;
+    uint32_t g = 0;
+    const int st = stream_grid(grid, bytes / 16, &g);
+    if (st != DF11_OK) return st;
+    hipLaunchKernelGGL(df11_stream_copy_kernel, dim3(g), dim3(kStreamThreads), 0,
+                       static_cast<hipStream_t>(hip_stream), static_cast<const u32x4 *>(src),
+                       static_cast<u32x4 *>(dst), bytes / 16);
+    return hipGetLastError() == hipSuccess ? DF11_OK : DF11_ERR_HIP;
+}

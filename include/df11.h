@@ -357,6 +357,26 @@ int df11_decode_gemm_noalloc(const df11_device_stream *s, const df11_gemv_matrix
 int df11_stream_ceiling(const uint8_t *a, const uint8_t *b, uint64_t b_bytes, uint16_t *out,
                         uint64_t n, uint32_t max_groups, void *hip_stream);
 
+/* Plain streams (measurement aids, not part of the decode path): the GPU's
+ * own read-only, write-only and copy rates, beside which the decode and the
+ * ceiling above are read.  bytes: a multiple of 16, above 0; src/dst: 16-byte
+ * aligned device pointers; 16-byte accesses, four in flight per thread, grid
+ * workgroups of 256 threads (0: 128 per compute unit; never more than the
+ * bytes need).  Enqueued on hip_stream.  Errors: ARG, HIP, and BUFSIZE for a
+ * short out.
+ *   df11_stream_read: reads src[0..bytes); thread t writes to out[t] the XOR
+ *     of the 32-bit words it read (so the XOR of all of out is the XOR of all
+ *     of src); out: device array of out_count uint32, at least
+ *     df11_stream_read_slots(bytes, grid) (0 for bad arguments).
+ *   df11_stream_write: fills dst[0..bytes) with 16-byte records {value,
+ *     value, value, record index (low 32 bits)}.
+ *   df11_stream_copy: dst[0..bytes) = src[0..bytes) (not overlapping). */
+uint32_t df11_stream_read_slots(uint64_t bytes, uint32_t grid);
+int df11_stream_read(const void *src, uint64_t bytes, uint32_t *out, uint64_t out_count,
+                     uint32_t grid, void *hip_stream);
+int df11_stream_write(void *dst, uint64_t bytes, uint32_t value, uint32_t grid, void *hip_stream);
+int df11_stream_copy(const void *src, void *dst, uint64_t bytes, uint32_t grid, void *hip_stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -295,3 +295,29 @@ def test_stream_ceiling_reads_every_byte(torch):
                 if g < groups:
                     want[g] ^= extra
     assert np.array_equal(got[:n].reshape(groups, 8), want)
+
+
+@pytest.mark.parametrize("nbytes,grid", [(16, 0), ((1 << 20) + 48, 0), ((5 << 20) + 4096, 7)])
+def test_plain_streams_do_what_they_say(torch, nbytes, grid):
+    """The read-only, write-only and copy streams (measurement aids): the copy
+    copies, the write writes its records, the read's per-thread XORs fold to
+    the XOR of everything read."""
+    n32 = nbytes // 4
+    src = torch.randint(-(1 << 31), (1 << 31) - 1, (n32 + 8,), dtype=torch.int32, device="cuda")
+    dst = torch.full((n32 + 8,), 7, dtype=torch.int32, device="cuda")
+    _say(f"[gpu] plain streams bytes={nbytes} grid={grid}")
+    hd.df11_stream_copy(src, dst, nbytes, grid)
+    torch.cuda.synchronize()
+    assert torch.equal(dst[:n32], src[:n32]) and bool((dst[n32:] == 7).all())
+    hd.df11_stream_write(dst, nbytes, 0x01020304, grid)
+    torch.cuda.synchronize()
+    rec = dst[:n32].view(-1, 4).cpu().numpy().astype(np.uint32)
+    assert (rec[:, :3] == 0x01020304).all()
+    assert (rec[:, 3] == np.arange(rec.shape[0], dtype=np.uint32)).all()
+    assert bool((dst[n32:] == 7).all())
+    slots = torch.full((hd.df11_stream_read_slots(nbytes, grid),), 5, dtype=torch.int32,
+                       device="cuda")
+    hd.df11_stream_read(src, slots, nbytes, grid)
+    torch.cuda.synchronize()
+    want = np.bitwise_xor.reduce(src[:n32].cpu().numpy().view(np.uint32))
+    assert np.bitwise_xor.reduce(slots.cpu().numpy().view(np.uint32)) == want

@@ -466,3 +466,19 @@ def test_tiled_workspace_size_and_refusal():
     bad = hd._mat_array(hd.gemv_matrices([(24, 4096), (40, 2048)])[0])
     assert lib.df11_decode_gemm_tiled(ctypes.byref(d), bad, 2, fake, fake, 2, 6144, fake, 96,
                                       fake, need, None) == -1
+
+
+def test_plain_streams_refuse_bad_arguments_before_any_device_call():
+    """The measurement-aid streams check sizes and alignment on the host."""
+    lib = hd.library()
+    ok, odd = 1 << 20, (1 << 20) + 8
+    assert lib.df11_stream_copy(ok, odd, 1024, 0, None) == -1      # misaligned dst
+    assert lib.df11_stream_copy(ok, ok, 1000, 0, None) == -1       # not a multiple of 16
+    assert lib.df11_stream_copy(ok, ok, 0, 0, None) == -1
+    assert lib.df11_stream_write(odd, 1024, 0, 0, None) == -1
+    assert lib.df11_stream_write(0, 1024, 0, 0, None) == -1
+    assert lib.df11_stream_read(ok, 1024, 0, 0, 0, None) == -1     # no out
+    assert lib.df11_stream_read(odd, 1024, ok, 1 << 20, 0, None) == -1
+    assert lib.df11_stream_read_slots(1000, 4) == 0
+    assert lib.df11_stream_read_slots(1 << 20, 4) == 4 * 256        # the grid given, 256 threads each
+    assert lib.df11_stream_read_slots(16, 4) == 256                 # never more than the bytes need
