@@ -132,20 +132,27 @@ def cpu_baseline(wlx, enc) -> dict:
         out[p0:p1] = oracle.join_bf16(e, enc.signmant[p0:p1])
         return e.size == p1 - p0
 
-    t0 = time.perf_counter()
+    # the threaded leg is short (a fraction of a second on a 218 M-weight
+    # block), so it runs five times and the median is reported
+    runs, okn = [], True
     with ThreadPoolExecutor(max_workers=threads) as pool:
-        sizes_ok = all(pool.map(chunk, range(len(edges) - 1)))
-    dtn = time.perf_counter() - t0
-    okn = sizes_ok and bool(np.array_equal(out, wlx.weights))
+        for _ in range(5):
+            out.fill(0)
+            t0 = time.perf_counter()
+            sizes_ok = all(pool.map(chunk, range(len(edges) - 1)))
+            runs.append(time.perf_counter() - t0)
+            okn = okn and sizes_ok and bool(np.array_equal(out, wlx.weights))
+    dtn = sorted(runs)[len(runs) // 2]
     return {"value": round((rd + wr) / dtn / 1e9, 4), "unit": "GB/s", "cores": threads,
             "kind": "oracle", "gweights_per_s": round(n / dtn / 1e9, 5),
-            "seconds": round(dtn, 3), "bit_exact": okn and ok1,
+            "seconds": round(dtn, 3), "seconds_of_5_runs": [round(t, 3) for t in runs],
+            "bit_exact": okn and ok1,
             "host_cpu_count": os.cpu_count(),
             "one_core": {"value": round((rd + wr) / dt1 / 1e9, 4), "unit": "GB/s", "cores": 1,
                          "gweights_per_s": round(n / dt1 / 1e9, 5), "seconds": round(dt1, 3)},
             "sample": f"whole {wlx.name} ({n} weights): oracle tree-walk decode of every "
                       f"code, then BF16 join; value: {len(edges) - 1} chunks of whole blocks "
-                      f"on {threads} threads; one_core: serial from bit 0"}
+                      f"on {threads} threads, median of 5 runs; one_core: serial from bit 0"}
 
 
 def run_copy(args) -> int:
