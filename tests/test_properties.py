@@ -13,28 +13,7 @@ from hypothesis import given, settings, strategies as st  # noqa: E402
 
 import huffman_decode_amd as hd  # noqa: E402
 import oracle  # noqa: E402
-
-
-@st.composite
-def bf16_words(draw):
-    n = draw(st.integers(1, 12_000))
-    seed = draw(st.integers(0, 2**31 - 1))
-    kind = draw(st.sampled_from(["geometric", "few", "subset", "any"]))
-    rng = np.random.default_rng(seed)
-    if kind == "any":
-        return rng.integers(0, 1 << 16, n, dtype=np.uint32).astype(np.uint16)
-    if kind == "geometric":  # long tails: codes up to the length limit
-        p = draw(st.floats(0.05, 0.95))
-        e = 127 - np.minimum(rng.geometric(p, n) - 1, 120)
-    elif kind == "few":
-        k = draw(st.integers(1, 3))
-        e = rng.choice(rng.integers(0, 256, k), n)
-    else:
-        k = draw(st.integers(2, 60))
-        pool = rng.choice(256, k, replace=False)
-        e = pool[np.minimum(rng.zipf(1.6, n) - 1, k - 1)]
-    sm = rng.integers(0, 256, n)
-    return (((sm & 0x80) << 8) | (e.astype(np.int64) << 7) | (sm & 0x7F)).astype(np.uint16)
+from gen_words import bf16_words  # noqa: E402
 
 
 @settings(max_examples=300, deadline=None, database=None)
