@@ -495,7 +495,8 @@ def fused_gemm(wlx, copies, stream, batch, reps=20) -> dict:
 
 def fused_tiled(wlx, stream, batches, n_copies=3, reps=20, warmup=300) -> dict:
     """y_b = W x_b for `batch` vectors on the matrix cores from the block
-    encoded in operand-tile order (df11_decode_gemm_tiled), timed over
+    encoded in operand-tile order (df11_decode_gemm_tiled), and the decode of
+    that stream back to row-major BF16 (df11_decode_tiled), timed over
     back-to-back launches on rotating copies like the decode."""
     import numpy as np
     import torch
@@ -505,8 +506,14 @@ def fused_tiled(wlx, stream, batches, n_copies=3, reps=20, warmup=300) -> dict:
     copies = [hd.tiled_to_device(te, "cuda") for _ in range(n_copies)]
     nx = max(m.x_offset + m.cols for m in te.mats)
     ny = sum(m.rows for m in te.mats)
-    rd, _ = algorithmic_bytes(te.enc)
+    rd, wr = algorithmic_bytes(te.enc)
     res = {}
+    # the decode of the same stream back to row-major BF16 (df11_decode_tiled)
+    out = torch.empty(te.enc.n, dtype=torch.int16, device="cuda")
+    ms = launch_time_ms(lambda k: hd.df11_decode_tiled(copies[k % n_copies], out, stream), stream,
+                        reps, warmup)
+    res["decode_row_major"] = {"ms": round(ms, 5), "gbs": round((rd + wr) / (ms * 1e-3) / 1e9, 1)}
+    del out
     for batch in batches:
         x = torch.from_numpy(np.random.default_rng(9).standard_normal((batch, nx)).astype(np.float32))
         x = x.cuda().to(torch.bfloat16)

@@ -120,6 +120,9 @@ def _load():
                                                ctypes.POINTER(GemvMatrix), _U32, _P, _P, _U32,
                                                _U64, _P, _U64, _P, _U64, _P]
         lib.df11_decode_gemm_tiled.restype = ctypes.c_int
+        lib.df11_decode_tiled.argtypes = [ctypes.POINTER(DeviceStream),
+                                          ctypes.POINTER(GemvMatrix), _U32, _P, _P]
+        lib.df11_decode_tiled.restype = ctypes.c_int
         lib.df11_tiled_workspace_bytes.argtypes = [ctypes.POINTER(GemvMatrix), _U32, _U32]
         lib.df11_tiled_workspace_bytes.restype = _U64
         lib.df11_stream_ceiling.argtypes = [_P, _P, _U64, _P, _U64, _U32, _P]
@@ -525,6 +528,21 @@ def df11_decode_gemm_tiled(td: TiledDevice, x, y, workspace=None, stream=None) -
     _check("df11_decode_gemm_tiled", _load().df11_decode_gemm_tiled(
         ctypes.byref(td.dev.desc), _mat_array(td.mats), len(td.mats), td.seg_blk.data_ptr(),
         x.data_ptr(), x.shape[0], x.stride(0), y.data_ptr(), y.stride(0), ws_ptr, ws_bytes,
+        stream.cuda_stream))
+
+
+def df11_decode_tiled(td: TiledDevice, out, stream=None) -> None:
+    """Enqueue the decode of a tile-order stream into ``out`` (a CUDA tensor of
+    at least n 16-bit elements), in the row-major order the weights had
+    before df11_tile_order."""
+    import torch
+    if out.element_size() != 2 or not out.is_contiguous() or out.numel() < td.dev.n:
+        raise ValueError("out must be a contiguous 16-bit tensor of at least n elements")
+    _same_device(td.dev, out=out)
+    if stream is None:
+        stream = torch.cuda.current_stream(out.device)
+    _check("df11_decode_tiled", _load().df11_decode_tiled(
+        ctypes.byref(td.dev.desc), _mat_array(td.mats), len(td.mats), out.data_ptr(),
         stream.cuda_stream))
 
 

@@ -431,6 +431,93 @@ struct StoreSink {  // plain decode: BF16 words to out[]
     __device__ __forceinline__ void end(uint32_t, uint32_t) {}
 };
 
+// Decode of a stream stored in operand-tile order back to the row-major
+// words.  The group of 8 words at tile-order position pos (tile t = pos >>
+// 9, lane group g = (pos >> 3) & 63) holds row 16 r + g % 16, columns 32 k +
+// 8 (g / 16) .. + 7 of its matrix, where r = u / ks and k = u % ks for u the
+// tile's index within the matrix (ks = cols / 32): 8 consecutive words of one
+// row, one 16-byte store.
+constexpr int kTileMapMats = 16;
+struct TileMap {
+    uint32_t n_mats;
+    uint32_t tile0[kTileMapMats + 1];  // each matrix's first tile; then the total
+    uint32_t ks[kTileMapMats];         // k-steps (cols / 32)
+    uint32_t cols[kTileMapMats];
+    uint64_t off[kTileMapMats];        // each matrix's first word
+};
+
+// The map in LDS, one 32-bit word per field: tile0[17], ks[16], cols[16],
+// off_lo[16], off_hi[16].
+constexpr int kTileMapWords = (kTileMapMats + 1) + 4 * kTileMapMats;
+
+struct TileStoreSink {
+    uint16_t *out;
+    const uint32_t *lmap;  // in LDS
+    uint32_t n_mats, lane;
+    struct Fetched {};
+    static constexpr int kEarlyFetch = 0;
+    static constexpr bool kRowPaths = false;
+    __device__ __forceinline__ bool one_row() const { return false; }
+    // the block's matrix when all its tiles are in one (the usual case)
+    bool single;
+    uint32_t m_tile0, m_ks, m_cols;
+    uint64_t m_off;
+    float m_inv;
+    __device__ __forceinline__ uint32_t tile0(uint32_t i) const { return lmap[i]; }
+    __device__ __forceinline__ uint32_t ks(uint32_t i) const { return lmap[kTileMapMats + 1 + i]; }
+    __device__ __forceinline__ uint32_t cols(uint32_t i) const {
+        return lmap[2 * kTileMapMats + 1 + i];
+    }
+    __device__ __forceinline__ uint64_t off(uint32_t i) const {
+        return lmap[3 * kTileMapMats + 1 + i] | ((uint64_t)lmap[4 * kTileMapMats + 1 + i] << 32);
+    }
+    // the matrix of tile t: the matrices 1.. starting at or before it (a
+    // search through the map in LDS, the same for every lane when t is)
+    __device__ __forceinline__ uint32_t matrix(uint32_t t) const {
+        uint32_t m = 0;
+        for (uint32_t i = 1; i < n_mats; ++i) m += t >= tile0(i) ? 1u : 0u;
+        return m;
+    }
+    __device__ __forceinline__ void begin(uint32_t p0, uint32_t p1, uint32_t, uint32_t, uint32_t) {
+        const uint32_t t0 = p0 >> 9, t1 = p1 > p0 ? (p1 - 1) >> 9 : t0;
+        const uint32_t m = __builtin_amdgcn_readfirstlane(matrix(t0));
+        m_tile0 = tile0(m), m_ks = ks(m), m_cols = cols(m), m_off = off(m);
+        single = t1 < tile0(m + 1);
+        m_inv = 1.0f / (float)m_ks;
+    }
+    // row-major index of the group at tile-order position pos (8-aligned)
+    __device__ __forceinline__ uint64_t where(uint32_t pos) const {
+        uint32_t t0 = m_tile0, k_steps = m_ks, c = m_cols;
+        uint64_t o = m_off;
+        float inv = m_inv;
+        const uint32_t t = pos >> 9, g = (pos >> 3) & 63u;
+        if (!single) {  // a block across matrices (small ones): each group looks its own up
+            const uint32_t m = matrix(t);
+            t0 = tile0(m), k_steps = ks(m), c = cols(m), o = off(m);
+            inv = 1.0f / (float)k_steps;
+        }
+        // u / k_steps through the reciprocal: u < 2^23, so the float quotient
+        // is off by at most one, and one step fixes it
+        const uint32_t u = t - t0;
+        uint32_t r = (uint32_t)((float)u * inv);
+        if ((uint64_t)r * k_steps > u) --r;
+        else if (u - r * k_steps >= k_steps) ++r;
+        const uint32_t k = u - r * k_steps;
+        return o + (uint64_t)(16 * r + (g & 15u)) * c + 32 * k + 8 * (g >> 4);
+    }
+    template <bool = false>
+    __device__ __forceinline__ Fetched fetch(uint32_t) const { return {}; }
+    template <bool = false>
+    __device__ __forceinline__ void group(uint32_t pos, uint2 e8, uint2 sm8, Fetched) {
+        *reinterpret_cast<uint4 *>(out + where(pos)) = join8(e8, sm8);
+    }
+    template <bool = false>
+    __device__ __forceinline__ void one(uint32_t pos, uint32_t e, uint32_t sm) {
+        out[where(pos & ~7u) + (pos & 7u)] = (uint16_t)join1(e, sm);
+    }
+    __device__ __forceinline__ void end(uint32_t, uint32_t) {}
+};
+
 // Fused product: y_b = W x_b for row-major matrices laid end to end in the
 // decoded output, for up to 8 input vectors x_b at once.  Every matrix row
 // holds at least 2048 words, so one block's output (at most 4096 words)
@@ -1005,6 +1092,32 @@ __device__ __forceinline__ void decode_blocks(const DecodeArgs &a, Sink &sink) {
 
 __global__ __launch_bounds__(kGroupThreads) DF11_OCCUPANCY_HINT void df11_decode_kernel(DecodeArgs a) {
     StoreSink sink{a.out};
+    decode_blocks(a, sink);
+}
+
+// The decode of a tile-order stream into row-major words.  Thread 0 copies
+// the map to LDS (constant indices into the kernel argument); the decode's
+// first workgroup barrier, after its table staging, orders the copy before
+// any block's use of it.
+__global__ __launch_bounds__(kGroupThreads) DF11_OCCUPANCY_HINT void df11_decode_tiled_kernel(
+    DecodeArgs a, TileMap m) {
+    __shared__ uint32_t lmap[kTileMapWords];
+    if (threadIdx.x == 0) {
+#pragma unroll
+        for (int i = 0; i <= kTileMapMats; ++i) lmap[i] = m.tile0[i];
+#pragma unroll
+        for (int i = 0; i < kTileMapMats; ++i) {
+            lmap[kTileMapMats + 1 + i] = m.ks[i];
+            lmap[2 * kTileMapMats + 1 + i] = m.cols[i];
+            lmap[3 * kTileMapMats + 1 + i] = (uint32_t)m.off[i];
+            lmap[4 * kTileMapMats + 1 + i] = (uint32_t)(m.off[i] >> 32);
+        }
+    }
+    TileStoreSink sink;
+    sink.out = a.out;
+    sink.lmap = lmap;
+    sink.n_mats = m.n_mats;
+    sink.lane = threadIdx.x % kWave;
     decode_blocks(a, sink);
 }
 
@@ -1689,7 +1802,8 @@ void df11_tiled_kernel(DecodeArgs a, TiledArgs t) {
 // Launch shape per device: compute units and, per kernel, resident
 // workgroups per CU for each table count (the LDS footprint depends on it).
 constexpr int kMaxDevices = 16;
-constexpr int kKernels = 5;  // 0: decode, 1..4: fused product for 1, 2, 4, 8 vectors
+// 0: decode, 1..4: fused product for 1, 2, 4, 8 vectors, 5: decode of a tile-order stream
+constexpr int kKernels = 6;
 std::atomic<int> g_cus[kMaxDevices];
 std::atomic<int> g_occ[kKernels][kMaxDevices][DF11_MAX_TABLES + 1];
 
@@ -1790,6 +1904,42 @@ extern "C" int df11_decode(const df11_device_stream *s, uint16_t *out, void *hip
     if (st != DF11_OK) return st;
     hipLaunchKernelGGL(df11_decode_kernel, dim3(groups), dim3(kGroupThreads),
                        lds_bytes(s->n_tables), static_cast<hipStream_t>(hip_stream), a);
+    return hipGetLastError() == hipSuccess ? DF11_OK : DF11_ERR_HIP;
+}
+
+extern "C" int df11_decode_tiled(const df11_device_stream *s, const df11_gemv_matrix *mats,
+                                 uint32_t n_mats, uint16_t *out, void *hip_stream) {
+    if (!out || !mats || n_mats < 1 || n_mats > (uint32_t)kTileMapMats) return DF11_ERR_ARG;
+    DecodeArgs a;
+    int st = prepare(s, out, &a);
+    if (st != DF11_OK) return st;
+    // the matrices in the tile layout: end to end from 0 over all n words,
+    // rows a multiple of 16, cols of 32
+    TileMap m = {};
+    m.n_mats = n_mats;
+    uint64_t off = 0;
+    for (uint32_t i = 0; i < n_mats; ++i) {
+        const df11_gemv_matrix &mm = mats[i];
+        if (mm.offset != off || mm.rows == 0 || mm.rows % 16 != 0 || mm.cols == 0 ||
+            mm.cols % 32 != 0)
+            return DF11_ERR_ARG;
+        m.tile0[i] = (uint32_t)(off / 512);
+        m.ks[i] = mm.cols / 32;
+        m.cols[i] = mm.cols;
+        m.off[i] = off;
+        off += (uint64_t)mm.rows * mm.cols;
+        if (off > s->n) return DF11_ERR_ARG;
+    }
+    if (off != s->n) return DF11_ERR_ARG;
+    for (uint32_t i = n_mats; i <= (uint32_t)kTileMapMats; ++i) m.tile0[i] = (uint32_t)(off / 512);
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return DF11_ERR_HIP;
+    int groups = 0;
+    st = launch_groups(df11_decode_tiled_kernel, 5, dev, s->n_tables, s->n_blocks, s->max_groups,
+                       &groups);
+    if (st != DF11_OK) return st;
+    hipLaunchKernelGGL(df11_decode_tiled_kernel, dim3(groups), dim3(kGroupThreads),
+                       lds_bytes(s->n_tables), static_cast<hipStream_t>(hip_stream), a, m);
     return hipGetLastError() == hipSuccess ? DF11_OK : DF11_ERR_HIP;
 }
 

@@ -319,6 +319,22 @@ int df11_decode_gemm_tiled(const df11_device_stream *s, const df11_gemv_matrix *
                            uint32_t batch, uint64_t x_stride, float *y, uint64_t y_stride,
                            void *workspace, uint64_t workspace_bytes, void *hip_stream);
 
+/* Decode of a stream in operand-tile order back to the row-major BF16 words
+ * the tile order was taken from (what df11_tile_order was given), for callers
+ * that keep only the tile-order encoding and need the weights themselves
+ * (more than 64 input vectors, other uses).  The decode is the one of
+ * df11_decode (page "DFloat11: lossless BFloat16 compression", sections
+ * "Architecture" and "How it works: the core algorithm"); each group of 8
+ * decoded words is 8 consecutive columns of one row and goes there with one
+ * 16-byte store.  mats, n_mats: as for df11_decode_gemm_tiled (1..16
+ * matrices, end to end from 0 over all n words, rows a multiple of 16, cols
+ * of 32; x and y offsets ignored).  out: device array of n BF16 words,
+ * 16-byte aligned, overwritten.  Corrupt blocks: as df11_decode.  Enqueued
+ * on hip_stream.  Errors: those of df11_decode, ARG for a matrix list that
+ * breaks the rules. */
+int df11_decode_tiled(const df11_device_stream *s, const df11_gemv_matrix *mats, uint32_t n_mats,
+                      uint16_t *out, void *hip_stream);
+
 /* Workspace bytes df11_decode_gemm_noalloc can use (32 MiB): enough for
  * batches 1-8 on the 218 M-weight Llama-3.1-8B-shaped block and batches 1-2 on
  * the 856 M-weight Llama-3.3-70B-shaped block. */

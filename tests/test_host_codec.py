@@ -482,3 +482,35 @@ def test_plain_streams_refuse_bad_arguments_before_any_device_call():
     assert lib.df11_stream_read_slots(1000, 4) == 0
     assert lib.df11_stream_read_slots(1 << 20, 4) == 4 * 256        # the grid given, 256 threads each
     assert lib.df11_stream_read_slots(16, 4) == 256                 # never more than the bytes need
+
+
+def test_decode_tiled_refuses_bad_matrix_lists_before_any_device_call():
+    """The tile-order decode takes 1..16 matrices laid end to end from 0 over
+    all n words, rows a multiple of 16 and cols of 32; anything else, or a
+    misaligned output, is refused on the host."""
+    lib = hd.library()
+    shapes = [(64, 4096), (32, 2048)]
+    n = sum(r * c for r, c in shapes)
+    te = hd.encode_tiled(wl.random_small(n, 4, "normal"), shapes)
+    sz = te.enc.sizes
+    d = hd.DeviceStream()
+    fake = 1 << 20
+    d.stream = d.gaps = d.block_pos = d.signmant = d.luts = fake
+    d.stream_bytes, d.gaps_bytes = sz.stream_bytes, sz.gaps_bytes
+    d.block_pos_count, d.signmant_bytes, d.lut_bytes = sz.block_pos_count, sz.signmant_bytes, \
+        sz.lut_bytes
+    d.n, d.total_bits, d.last_start = sz.n, sz.total_bits, sz.last_start
+    d.n_blocks, d.n_tables, d.max_len = sz.n_blocks, te.enc.codebook.n_tables, \
+        te.enc.codebook.max_len
+    call = lambda mats, count, out=fake: lib.df11_decode_tiled(
+        ctypes.byref(d), hd._mat_array(mats), count, out, None)
+    mats = te.mats
+    assert call(mats, 0) == -1                                   # no matrices
+    assert call(mats, 1) == -1                                   # does not cover n
+    assert call(mats, 2, fake + 8) == -1                         # output not 16-byte aligned
+    assert call(hd.gemv_matrices([(24, 4096), (40, 2048)])[0], 2) == -1   # rows % 16
+    assert call(hd.gemv_matrices([(64, 4080), (32, 2064)])[0], 2) == -1   # cols % 32
+    gap = [hd.GemvMatrix(0, 64, 4096, 0, 0), hd.GemvMatrix(64 * 4096 + 512, 32, 2048, 0, 64)]
+    assert call(gap, 2) == -1                                    # not end to end
+    many = hd.gemv_matrices([(16, 32)] * 17)[0]
+    assert call(many, 17) == -1                                  # more than 16
