@@ -538,8 +538,25 @@ def run_tiled(args) -> int:
     torch.cuda.set_device(dev)
     wlx = wl.CONFIGS[args.workload]()
     batches = [int(b) for b in args.batches.split(",")]
-    res = fused_tiled(wlx, torch.cuda.current_stream(dev), batches, reps=args.steps,
-                      warmup=args.warmup)
+    stream = torch.cuda.current_stream(dev)
+    res = fused_tiled(wlx, stream, batches, reps=args.steps, warmup=args.warmup)
+    if args.decode_cols:
+        # the row-major decode of the same words laid out as one matrix of
+        # each width: at 32 columns a tile is 1 KB of contiguous output, from
+        # 64 on each tile writes 64 bytes of each of its 16 rows
+        import huffman_decode_amd as hd
+        rd, wr = algorithmic_bytes(hd.encode(wlx.weights))
+        for c in (int(v) for v in args.decode_cols.split(",")):
+            if wlx.n % (16 * c):
+                raise SystemExit(f"{wlx.n} weights do not make {c}-column rows in 16-row tiles")
+            te = hd.encode_tiled(wlx.weights, [(wlx.n // c, c)])
+            td = hd.tiled_to_device(te, "cuda")
+            out = torch.empty(wlx.n, dtype=torch.int16, device="cuda")
+            ms = launch_time_ms(lambda k: hd.df11_decode_tiled(td, out, stream), stream,
+                                args.steps, args.warmup)
+            res[f"decode_cols{c}"] = {"ms": round(ms, 5),
+                                      "gbs": round((rd + wr) / (ms * 1e-3) / 1e9, 1)}
+            del td, out
     print(json.dumps({"mode": "tiled", "workload": args.workload, "steps": args.steps,
                       "warmup": args.warmup, **res}), flush=True)
     return 0
@@ -639,6 +656,9 @@ def main() -> int:
                          "offload: blocks from pinned host memory, copied and decoded in turn")
     ap.add_argument("--layers", type=int, default=32, help="blocks in the stack mode")
     ap.add_argument("--batches", default="1,16,64", help="vectors per call in the tiled mode")
+    ap.add_argument("--decode-cols", default="",
+                    help="tiled mode: also time the row-major decode of the workload's words "
+                         "laid out as one matrix of each of these widths (comma separated)")
     ap.add_argument("--copy-mib", type=int, default=1024)
     args = ap.parse_args()
     fast = args.mode in ("decode", "copy", "ceiling", "stream")
