@@ -32,7 +32,7 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E peak (vendor figure)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "df11_decode_llama8b_block_traffic.txt")
 
 
-def kernel_hash(name: str = "df11_decode_kernel") -> str | None:
+def kernel_hash(name: str = "df11_decode_kernel<32>") -> str | None:
     """Hash of a kernel's machine code in the built library (written by the
     build next to it): counters stay valid exactly as long as it is equal."""
     path = os.path.join(ROOT, "huffman_decode_amd", "libdf11.kernels.json")

@@ -61,36 +61,50 @@ constexpr int kWave = 64;
 constexpr int kWavesPerGroup = 8;
 constexpr int kGroupThreads = kWave * kWavesPerGroup;
 constexpr int kMaxBlockCodes = DF11_BLOCK_SLICES * DF11_SLICE_BITS;  // all 1-bit codes
-// staging: lane t's phase-1 exponents at byte 4 + 40 t of its wave's LDS
-// region (the 4 bytes in front let every lane read the dword before its slot);
-// a lane with more than 32 codes, or with fewer than 3 before the block's last
-// code, sends the wave to the re-decode route
+// Staging: lane t's phase-1 exponents at byte 4 + t * stride of its wave's
+// LDS region (the 4 bytes in front let every lane read the dword before its
+// slot); a lane with more than kCodes codes, or with fewer than 3 before the
+// block's last code, sends the wave to the re-decode route.  The tile that
+// phase 2 fills reuses the region.  32 codes per lane serve every stream of
+// ordinary weights (about 24 codes of 2.6 bits per 64-bit slice); streams of
+// much shorter codes get 56, with a larger region and fewer workgroups per
+// CU.
 constexpr int kStageBase = 4;
-constexpr int kStageStride = 40;
-constexpr int kStageCodes = 32;
 constexpr int kStageMinCodes = 3;
-// exponent bytes one tile holds (the tile reuses the wave's staging region);
-// blocks with more symbols take several passes
-constexpr int kTileCap = 2560;
 // phase 1 writes at most 71 bytes from a slot's start, whatever the data: a
 // step begins below bit 64 and every code takes at least one bit, so the
 // last step begins after at most 63 codes and stores two aligned dwords
 constexpr int kStageReach = 63 + 8;
-constexpr int kTileBytes = kTileCap + 40;
-static_assert(kTileCap % 8 == 0, "tile windows must stay 8-aligned");
-static_assert(kTileBytes >= kStageBase + 63 * kStageStride + kStageReach, "staging must fit");
-static_assert(kStageStride % 4 == 0 && kStageBase % 4 == 0 && kTileBytes % 8 == 0,
-              "staging dwords are aligned");
-static_assert(kStageStride >= kStageCodes + 4, "a full slot takes 4 stray bytes");
+template <int kCodes> struct StageGeo {
+    static constexpr int kStageCodes = kCodes;
+    static constexpr int kStageStride = kCodes + 8;
+    // the wave's region: all 64 slots, 8-aligned
+    static constexpr int kTileBytes = (kStageBase + 63 * kStageStride + kStageReach + 7) / 8 * 8;
+    // exponent bytes one tile holds; blocks with more symbols take several passes
+    static constexpr int kTileCap = kTileBytes - 40;
+    static constexpr int kTilesBytes = 8 * kTileBytes;
+    static_assert(kTileCap % 8 == 0, "tile windows must stay 8-aligned");
+    static_assert(kStageStride % 4 == 0 && kTileBytes % 8 == 0, "staging dwords are aligned");
+    static_assert(kStageStride >= kStageCodes + 4, "a full slot takes 4 stray bytes");
+    static_assert(kCodes % 4 == 0, "slots move in whole dwords");
+    static_assert(kTilesBytes < 0x10000, "tile addresses must fit 16 bits");
+};
+using NarrowGeo = StageGeo<32>;
+using WideGeo = StageGeo<56>;
+constexpr int kStageStride = NarrowGeo::kStageStride;
+constexpr int kStageCodes = NarrowGeo::kStageCodes;
+constexpr int kTileCap = NarrowGeo::kTileCap;
+constexpr int kTileBytes = NarrowGeo::kTileBytes;
+static_assert(kTileCap == 2560 && kTileBytes == 2600, "the narrow geometry");
 constexpr int kTableBytes = 256 * 2;
 constexpr int kXcds = 8;
 // multi-code decode table (built by the host after the 8-bit tables of the
 // table image, copied to LDS by each workgroup): index width
 constexpr int kDecodeBits = (int)df11_internal::kDecodeTableBits;
 constexpr int kDecodeBytes = (int)df11_internal::kDecodeTableBytes;
-constexpr int kTilesBytes = kWavesPerGroup * kTileBytes;
+static_assert(kWavesPerGroup == 8, "one region per wave of a workgroup");
+constexpr int kTilesBytes = NarrowGeo::kTilesBytes;
 constexpr int kStaticLds = kTilesBytes + kDecodeBytes;
-static_assert(kTilesBytes < 0x10000, "tile addresses must fit 16 bits");
 // sign|mantissa groups of 8 per lane loaded up front
 constexpr int kPrefetchGroups = 2;
 static_assert(kPrefetchGroups >= 1, "at least one group is prefetched");
@@ -259,19 +273,21 @@ __device__ __forceinline__ uint32_t stage_codes(const uint8_t *lds_dec, const ui
     return (acc >> 16) - slot;
 }
 
-// After the scan: move the lane's `cnt` staged exponents (at most 32) from its
+// After the scan: move the lane's `cnt` staged exponents (at most kStageCodes) from its
 // slot to tile address `dst` with aligned dword stores only.  The lane writes
 // every aligned dword that ends inside its own output bytes; the first of
 // them starts with the previous lane's last bytes (`prev`, taken from that
 // lane's slot), and the lane holding the block's last code (`last_lane`) also
 // writes its final, partial dword.  Every tile dword is thus written exactly
 // once, provided each lane before the last one holds at least 3 codes.
+template <class G = NarrowGeo>
 __device__ __forceinline__ void place_staged(uint32_t slot, uint32_t dst, uint32_t cnt,
                                              uint32_t prev, bool last_lane) {
-    uint32_t v[9];
+    constexpr int kN = G::kStageCodes / 4;
+    uint32_t v[kN + 1];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = *(const lds_u32 *)(uintptr_t)(slot + 4 * i);
-    v[8] = 0;
+    for (int i = 0; i < kN; ++i) v[i] = *(const lds_u32 *)(uintptr_t)(slot + 4 * i);
+    v[kN] = 0;
     const uint32_t s = dst & 3u, a0 = dst & ~3u;
     // byte t of output dword j is byte 4 j + t - s of the lane's sequence;
     // v_perm picks it from {v[j], v[j - 1]} (bytes 4..7 and 0..3)
@@ -280,7 +296,7 @@ __device__ __forceinline__ void place_staged(uint32_t slot, uint32_t dst, uint32
                      : last_lane ? (int)((s + cnt - 1) >> 2)
                                  : (int)((s + cnt) >> 2) - 1;
 #pragma unroll
-    for (int j = 0; j < 9; ++j) {
+    for (int j = 0; j <= kN; ++j) {
         const uint32_t val = __builtin_amdgcn_perm(v[j], j ? v[j - 1] : prev, sel);
         if (j <= last) *(lds_u32 *)(uintptr_t)(a0 + 4 * j) = val;
     }
@@ -309,7 +325,7 @@ __device__ __forceinline__ uint32_t staged_tail(uint32_t slot, uint32_t cnt) {
 // are harmless.  rewrite_head() then restores every lane's first symbols.
 // With kRanged only positions in [r0, r0 + kTileCap) are stored, at
 // tile[position - r0], one checked slot at a time.
-template <bool kRanged>
+template <bool kRanged, class G = NarrowGeo>
 __device__ __forceinline__ void decode_codes(const uint8_t *lds_dec, const uint16_t *lut,
                                              uint32_t n_tables, uint32_t d0, uint32_t d1,
                                              uint32_t d2, uint32_t pos, uint32_t stop,
@@ -319,7 +335,7 @@ __device__ __forceinline__ void decode_codes(const uint8_t *lds_dec, const uint1
     constexpr uint32_t kMask = ((1u << kDecodeBits) - 1) << 3;
     // pos | (LDS address of the next exponent byte) << 16; ranged: position << 16
     uint32_t acc = pos | ((kRanged ? at : tile_addr + at) << 16);
-    const uint32_t tile_end = tile_addr + kTileBytes - 4;  // last 4-byte store address
+    const uint32_t tile_end = tile_addr + G::kTileBytes - 4;  // last 4-byte store address
     const uint32_t stop0 = stop < 32u ? stop : 32u;
     auto step = [&](uint32_t hi, uint32_t lo, uint32_t dhi, uint32_t dlo) {
         const uint32_t w = __builtin_amdgcn_alignbit(hi, lo, acc);
@@ -354,7 +370,7 @@ __device__ __forceinline__ void decode_codes(const uint8_t *lds_dec, const uint1
             const uint32_t p = (acc >> 16) - k;  // position of the first symbol
             for (uint32_t j = 0; j < 4; ++j) {
                 const uint32_t rel = p + j - r0;
-                if (j < k && rel < (uint32_t)kTileCap)
+                if (j < k && rel < (uint32_t)G::kTileCap)
                     *((lds_u8 *)(uintptr_t)(tile_addr + rel)) = (uint8_t)(syms >> (8 * j));
             }
         }
@@ -752,22 +768,22 @@ struct DotSink {
 // most that still lets 3 workgroups of 8 waves share a CU
 constexpr int kWavesPerEu = 6;
 #define DF11_OCCUPANCY_HINT __attribute__((amdgpu_waves_per_eu(kWavesPerEu)))
-template <class Sink>
+template <class G, class Sink>
 __device__ __forceinline__ void decode_blocks(const DecodeArgs &a, Sink &sink) {
     // LDS: per-wave regions (staging slots, then the exponent tile) | decode
     // table in one static array (fixed offsets fold into the ds_read/ds_write
     // immediates, and the regions sit at the lowest addresses so that their
     // addresses fit the 16-bit field of the phase accumulators), then the 8-bit
     // tables in dynamic LDS.
-    __shared__ __attribute__((aligned(16))) uint8_t lds_static[kStaticLds];
+    __shared__ __attribute__((aligned(16))) uint8_t lds_static[G::kTilesBytes + kDecodeBytes];
     __shared__ uint32_t wg_next;  // next block index of this workgroup's share
     if (threadIdx.x == 0) wg_next = kWavesPerGroup;  // claims 0..7: one per wave, below
     uint8_t *tiles = lds_static;
-    uint2 *dec_t = reinterpret_cast<uint2 *>(lds_static + kTilesBytes);
+    uint2 *dec_t = reinterpret_cast<uint2 *>(lds_static + G::kTilesBytes);
     extern __shared__ uint4 smem_u4[];
     uint16_t *lut = reinterpret_cast<uint16_t *>(smem_u4);
     const uint32_t hier_bytes = a.n_tables * kTableBytes;
-    if (lds_offset(tiles) + kTilesBytes > 0x10000u) {
+    if (lds_offset(tiles) + G::kTilesBytes > 0x10000u) {
         // tile addresses would not fit the accumulator: decode nothing
         if (threadIdx.x == 0 && a.status) atomicAdd(a.status, 1u);
         return;
@@ -775,7 +791,7 @@ __device__ __forceinline__ void decode_blocks(const DecodeArgs &a, Sink &sink) {
 
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const uint32_t lane = threadIdx.x % kWave;
-    uint8_t *tile = tiles + wave * kTileBytes;
+    uint8_t *tile = tiles + wave * G::kTileBytes;
     const uint32_t tile_addr = lds_offset(tile);
     const uint8_t *lds_dec = reinterpret_cast<const uint8_t *>(dec_t);
 
@@ -873,7 +889,7 @@ __device__ __forceinline__ void decode_blocks(const DecodeArgs &a, Sink &sink) {
         const bool sane = p1 >= p0 && p1 <= a.n && p1 - p0 <= (uint32_t)kMaxBlockCodes;
         const uint32_t base = p0 & ~7u;
         const uint32_t groups = sane ? (p1 - base + 7) >> 3 : 0u;
-        const bool one_pass = groups * 8 + 4 <= (uint32_t)kTileCap;
+        const bool one_pass = groups * 8 + 4 <= (uint32_t)G::kTileCap;
         // groups [full_lo, full_hi) lie inside [p0, p1) and get 16-byte stores;
         // the partial head group (p0 unaligned) and tail group (p1 unaligned)
         // are stored one element per lane: lanes 0-7 the head, 8-15 the tail
@@ -950,7 +966,7 @@ __device__ __forceinline__ void decode_blocks(const DecodeArgs &a, Sink &sink) {
         }
 
         // ---- phase 1: decode into the lane's staging slot, counting
-        const uint32_t slot = tile_addr + kStageBase + lane * kStageStride;
+        const uint32_t slot = tile_addr + kStageBase + lane * G::kStageStride;
         const uint32_t cnt =
             lim ? stage_codes(lds_dec, lut, a.n_tables, d0, d1, d2, f0, f1, f2, gap, lim, slot)
                 : 0u;
@@ -990,7 +1006,7 @@ __device__ __forceinline__ void decode_blocks(const DecodeArgs &a, Sink &sink) {
         // every lane's codes fit its slot (then the block fits one tile, too)
         // and every lane before the last code holds enough for its neighbour
         const bool last_lane = incl == total;
-        const bool odd = cnt > (uint32_t)kStageCodes || (cnt < (uint32_t)kStageMinCodes && !last_lane);
+        const bool odd = cnt > (uint32_t)G::kStageCodes || (cnt < (uint32_t)kStageMinCodes && !last_lane);
         const bool staged = one_pass && __builtin_amdgcn_ballot_w64(odd) == 0;
 
         wave_lds_sync();
@@ -999,12 +1015,12 @@ __device__ __forceinline__ void decode_blocks(const DecodeArgs &a, Sink &sink) {
             const uint32_t tail = staged_tail(slot, cnt);
             const uint32_t prev = (uint32_t)__builtin_amdgcn_ds_bpermute(
                 (int)(((lane + kWave - 1) % kWave) * 4), (int)tail);
-            place_staged(slot, tile_addr + at, cnt, prev, last_lane);
+            place_staged<G>(slot, tile_addr + at, cnt, prev, last_lane);
             wave_lds_sync();
         } else if (one_pass) {
             // ---- phase 2: decode the real bits again into the tile, then
             // restore each lane's head
-            decode_codes<false>(lds_dec, lut, a.n_tables, d0, d1, d2, start, stop, tile_addr, at, 0);
+            decode_codes<false, G>(lds_dec, lut, a.n_tables, d0, d1, d2, start, stop, tile_addr, at, 0);
             wave_lds_sync();
             rewrite_head(lds_dec, lut, a.n_tables, d0, d1, d2, start, cnt, tile_addr + at);
             wave_lds_sync();
@@ -1070,11 +1086,11 @@ __device__ __forceinline__ void decode_blocks(const DecodeArgs &a, Sink &sink) {
             wave_lds_sync();
         } else {
             // more symbols than one tile holds: decode again per tile-sized window
-            for (uint32_t r0 = 0; r0 < groups * 8; r0 += kTileCap) {
-                decode_codes<true>(lds_dec, lut, a.n_tables, d0, d1, d2, start, stop, tile_addr,
+            for (uint32_t r0 = 0; r0 < groups * 8; r0 += G::kTileCap) {
+                decode_codes<true, G>(lds_dec, lut, a.n_tables, d0, d1, d2, start, stop, tile_addr,
                                    at, r0);
                 wave_lds_sync();
-                const uint32_t j_hi = (r0 + kTileCap) / 8 < groups ? (r0 + kTileCap) / 8 : groups;
+                const uint32_t j_hi = (r0 + G::kTileCap) / 8 < groups ? (r0 + G::kTileCap) / 8 : groups;
                 for (uint32_t j = r0 / 8 + lane; j < j_hi; j += kWave) {
                     if (j < full_lo || j >= full_hi) continue;  // edge groups: below
                     const uint2 sm = load_sm8(a.signmant + base + 8 * j);
@@ -1082,7 +1098,7 @@ __device__ __forceinline__ void decode_blocks(const DecodeArgs &a, Sink &sink) {
                                sink.fetch(base + 8 * j));
                 }
                 const uint32_t er = edge_i - base - r0;
-                if (edge && er < (uint32_t)kTileCap) sink.one(edge_i, tile[er], edge_sm);
+                if (edge && er < (uint32_t)G::kTileCap) sink.one(edge_i, tile[er], edge_sm);
                 wave_lds_sync();
             }
         }
@@ -1090,9 +1106,10 @@ __device__ __forceinline__ void decode_blocks(const DecodeArgs &a, Sink &sink) {
     }
 }
 
+template <int kCodes>
 __global__ __launch_bounds__(kGroupThreads) DF11_OCCUPANCY_HINT void df11_decode_kernel(DecodeArgs a) {
     StoreSink sink{a.out};
-    decode_blocks(a, sink);
+    decode_blocks<StageGeo<kCodes>>(a, sink);
 }
 
 // The decode of a tile-order stream into row-major words.  Thread 0 copies
@@ -1118,7 +1135,7 @@ __global__ __launch_bounds__(kGroupThreads) DF11_OCCUPANCY_HINT void df11_decode
     sink.lmap = lmap;
     sink.n_mats = m.n_mats;
     sink.lane = threadIdx.x % kWave;
-    decode_blocks(a, sink);
+    decode_blocks<NarrowGeo>(a, sink);
 }
 
 // Occupancy of the fused product kernel for capacity kB.  Up to 2 vectors
@@ -1160,7 +1177,7 @@ void df11_gemm_kernel(DecodeArgs a, GemvArgs g) {
     sink.batch = g.batch;
     sink.n_mats = g.n_mats;
     sink.lane = threadIdx.x % kWave;
-    decode_blocks(a, sink);
+    decode_blocks<NarrowGeo>(a, sink);
 }
 
 // y of every row and vector: the sums its blocks stored, in block order.
@@ -1802,8 +1819,9 @@ void df11_tiled_kernel(DecodeArgs a, TiledArgs t) {
 // Launch shape per device: compute units and, per kernel, resident
 // workgroups per CU for each table count (the LDS footprint depends on it).
 constexpr int kMaxDevices = 16;
-// 0: decode, 1..4: fused product for 1, 2, 4, 8 vectors, 5: decode of a tile-order stream
-constexpr int kKernels = 6;
+// 0: decode, 1..4: fused product for 1, 2, 4, 8 vectors, 5: decode of a tile-order stream,
+// 6: decode with 56-code staging slots
+constexpr int kKernels = 7;
 std::atomic<int> g_cus[kMaxDevices];
 std::atomic<int> g_occ[kKernels][kMaxDevices][DF11_MAX_TABLES + 1];
 
@@ -1848,6 +1866,18 @@ int launch_groups(K kernel, int which, int dev, uint32_t n_tables, uint32_t n_bl
     g = (g + kXcds - 1) / kXcds * kXcds;
     *groups = (int)g;
     return DF11_OK;
+}
+
+// The plain decode stages up to 56 codes per lane (instead of 32) for a
+// stream whose codes average under 64 / 30 = 2.13 bits: 30 or more codes
+// start in a 64-bit slice, and nearly every block holds a lane with more than
+// 32 (ordinary BF16 weights average 2.6-2.8 bits, 23-25 codes per slice).
+// The wider slots cost a workgroup per CU (3 instead of 4), which outweighs
+// the re-decode route for streams a little above 25 codes per slice: that
+// route is the cheaper of the two there.  Either kernel decodes every stream;
+// the choice only decides which blocks take the re-decode route.
+bool uses_wide_slots(const df11_device_stream *s) {
+    return 64 * (unsigned __int128)s->n > 30 * (unsigned __int128)s->total_bits;
 }
 
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -1900,10 +1930,21 @@ extern "C" int df11_decode(const df11_device_stream *s, uint16_t *out, void *hip
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return DF11_ERR_HIP;
     int groups = 0;
-    st = launch_groups(df11_decode_kernel, 0, dev, s->n_tables, s->n_blocks, s->max_groups, &groups);
-    if (st != DF11_OK) return st;
-    hipLaunchKernelGGL(df11_decode_kernel, dim3(groups), dim3(kGroupThreads),
-                       lds_bytes(s->n_tables), static_cast<hipStream_t>(hip_stream), a);
+    if (uses_wide_slots(s)) {
+        st = launch_groups(df11_decode_kernel<WideGeo::kStageCodes>, 6, dev, s->n_tables,
+                           s->n_blocks, s->max_groups, &groups);
+        if (st != DF11_OK) return st;
+        hipLaunchKernelGGL(df11_decode_kernel<WideGeo::kStageCodes>, dim3(groups),
+                           dim3(kGroupThreads), lds_bytes(s->n_tables),
+                           static_cast<hipStream_t>(hip_stream), a);
+    } else {
+        st = launch_groups(df11_decode_kernel<NarrowGeo::kStageCodes>, 0, dev, s->n_tables,
+                           s->n_blocks, s->max_groups, &groups);
+        if (st != DF11_OK) return st;
+        hipLaunchKernelGGL(df11_decode_kernel<NarrowGeo::kStageCodes>, dim3(groups),
+                           dim3(kGroupThreads), lds_bytes(s->n_tables),
+                           static_cast<hipStream_t>(hip_stream), a);
+    }
     return hipGetLastError() == hipSuccess ? DF11_OK : DF11_ERR_HIP;
 }
 

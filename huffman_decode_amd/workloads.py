@@ -216,7 +216,10 @@ def all_exponents(seed: int = 5004, rows: int = 4096, cols: int = 4096) -> Workl
 
 
 def random_small(n: int, seed: int, kind: str = "normal") -> np.ndarray:
-    """Small flat tensors for edge cases: 'normal', 'single', 'uniform', 'int8'."""
+    """Small flat tensors for edge cases: 'normal', 'single', 'uniform', 'int8',
+    and 'geometric' / 'geometric_steep': exponent 127 - j with probability
+    proportional to 0.45^j / 0.3^j (codes of about 2 / 1.4 bits on average,
+    so 30-45 codes start in a 64-bit slice), random sign|mantissa."""
     rng = np.random.default_rng(seed)
     if kind == "normal":
         return to_bf16((rng.standard_normal(n) * 0.02).astype(np.float32))
@@ -227,6 +230,11 @@ def random_small(n: int, seed: int, kind: str = "normal") -> np.ndarray:
         return rng.integers(0, 1 << 16, n, dtype=np.uint16).astype(np.uint16)
     if kind == "int8":
         return to_bf16((rng.integers(-127, 128, n) * (0.02 / 127)).astype(np.float32))
+    if kind in ("geometric", "geometric_steep"):
+        q = 0.45 if kind == "geometric" else 0.3
+        j = np.minimum(rng.geometric(1.0 - q, n) - 1, 120).astype(np.uint16)
+        low = rng.integers(0, 256, n, dtype=np.uint16)
+        return (((low & 0x80) << 8) | ((127 - j) << 7) | (low & 0x7F)).astype(np.uint16)
     raise ValueError(kind)
 
 

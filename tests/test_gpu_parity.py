@@ -65,6 +65,10 @@ SMALL = [
     ("single_5000", lambda: wl.random_small(5000, 10, "single")),
     ("single_full_tiles", lambda: wl.random_small(4096 * 70 + 3, 11, "single")),
     ("uniform_300001", lambda: wl.random_small(300_001, 12, "uniform")),
+    # codes of 1.4-2 bits: the 56-code staging slots, staged and fallback blocks
+    ("geometric_1000003", lambda: wl.random_small(1_000_003, 16, "geometric")),
+    ("geometric_steep_700001", lambda: wl.random_small(700_001, 17, "geometric_steep")),
+    ("geometric_4097", lambda: wl.random_small(4097, 18, "geometric")),
     ("int8_200000", lambda: wl.random_small(200_000, 13, "int8")),
     ("all_exponents_small", lambda: wl.all_exponents(14, 256, 1024).weights),
     ("flux_small", lambda: wl.flux_block(15, scale=1 / 64).weights),
@@ -100,7 +104,8 @@ def test_full_size_configs(torch, name):
 
 
 @pytest.mark.parametrize("kind,n,seed", [("normal", 300_000, 31), ("single", 4096 * 40, 32),
-                                          ("uniform", 200_000, 33)])
+                                          ("uniform", 200_000, 33), ("geometric", 400_000, 34),
+                                          ("geometric_steep", 300_000, 35)])
 def test_flipped_stream_bits_stay_in_their_blocks(torch, kind, n, seed):
     """A flipped stream bit desynchronises the codes of its slice (the pages'
     failure mode).  A lane also reads 32 bits into the next slice, so a flip

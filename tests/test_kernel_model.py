@@ -8,11 +8,12 @@ the originals, so a logic error in the kernel's scheme shows up without a GPU:
 * phase 1 on the slice bits with everything after the lane's last code forced
   to one: every step stores four symbol bytes into the lane's private staging
   slot (stray bytes included), and the step count gives the exact code count;
-* the wave scan and, when every lane holds 3 to 32 codes (or is past the
-  block's last code), the placement: each lane writes the aligned tile dwords
-  that end inside its own output bytes, the first one completed with the
-  previous lane's last bytes, the lane holding the block's last code also its
-  final partial dword; every tile dword is written exactly once;
+* the wave scan and, when every lane holds 3 to 32 codes (56 in the wide
+  geometry for streams of short codes) or is past the block's last code, the
+  placement: each lane writes the aligned tile dwords that end inside its own
+  output bytes, the first one completed with the previous lane's last bytes,
+  the lane holding the block's last code also its final partial dword; every
+  tile dword is written exactly once;
 * otherwise the fallback: phase 2 decodes the real bits again straight into
   the tile, then every lane's first symbols are decoded and stored again.
 """
@@ -24,12 +25,15 @@ from huffman_decode_amd import workloads as wl
 
 DECODE_BITS = 11
 MAX_SYMS = 4
-STAGE_STRIDE = 40      # bytes of staging per lane
-STAGE_BASE = 4         # lane t's slot starts at byte 4 + 40 t of the region
-STAGE_CODES = 32       # codes a lane may stage; more sends the wave to the fallback
+STAGE_BASE = 4         # lane t's slot starts at byte 4 + stride t of the region
 MIN_CODES = 3          # fewer (before the block's last code) also does
-REGION = 2600          # LDS bytes per wave (staging and tile share them)
-TILE_CAP = 2560
+# staging geometries: codes a lane may stage (more sends the wave to the
+# fallback), bytes of staging per lane, LDS bytes per wave (staging and tile
+# share them), exponent bytes one tile holds.  The kernel stages 32 codes per
+# lane, and 56 for streams whose codes average under 2.13 bits.
+NARROW = dict(codes=32, stride=40, region=2600, cap=2560)
+WIDE = dict(codes=56, stride=64, region=4112, cap=4072)
+TILE_CAP = NARROW["cap"]
 STRAY = 0xEE           # value of the unfilled slots of a decode entry in this model
 
 
@@ -91,7 +95,7 @@ def _walk(ln, bits, dec_t, lut, n_tables, mem, at):
     return k
 
 
-def _model_block(enc, b, dec_t, lut):
+def _model_block(enc, b, dec_t, lut, geo=NARROW):
     s = enc.sizes
     n_tables = enc.codebook.n_tables
     bits = np.unpackbits(enc.stream, bitorder="little")
@@ -113,11 +117,11 @@ def _model_block(enc, b, dec_t, lut):
         lanes.append(dict(gap=gap, lim=lim, bits=slice_bits, padded=padded))
 
     # the wave's LDS region; garbage to start with
-    mem = np.full(REGION + 8, 0x77, np.int32)
+    mem = np.full(geo["region"] + 8, 0x77, np.int32)
     # phase 1 in lane order 63..0 so that overflowing lanes' stores land last
     for lane in range(63, -1, -1):
         ln = lanes[lane]
-        slot = STAGE_BASE + STAGE_STRIDE * lane
+        slot = STAGE_BASE + geo["stride"] * lane
         ln["cnt"] = _walk(ln, ln["padded"], dec_t, lut, n_tables, mem, slot) if ln["lim"] else 0
     counts = [ln["cnt"] for ln in lanes]
     assert sum(counts) == p1 - p0
@@ -125,15 +129,15 @@ def _model_block(enc, b, dec_t, lut):
     excl = incl - counts
     total = int(incl[-1])
     groups = (p1 - base + 7) >> 3
-    bad = [c > STAGE_CODES or (c < MIN_CODES and incl[l] != total) for l, c in enumerate(counts)]
+    bad = [c > geo["codes"] or (c < MIN_CODES and incl[l] != total) for l, c in enumerate(counts)]
 
-    if not any(bad) and groups * 8 + 4 <= TILE_CAP:
-        # every lane reads its 8 staged dwords and the 4 bytes ending at its
+    if not any(bad) and groups * 8 + 4 <= geo["cap"]:
+        # every lane reads its codes / 4 staged dwords and the 4 bytes ending at its
         # last code (from its slot, before anything is written)
         staged, tail4 = [], []
         for lane in range(64):
-            slot = STAGE_BASE + STAGE_STRIDE * lane
-            staged.append([int(x) for x in mem[slot: slot + 32]] + [0, 0, 0, 0])
+            slot = STAGE_BASE + geo["stride"] * lane
+            staged.append([int(x) for x in mem[slot: slot + geo["codes"]]] + [0, 0, 0, 0])
             b = counts[lane] - 4
             tail4.append([int(x) for x in mem[slot + b: slot + b + 4]])
         written = np.zeros(mem.size, bool)
@@ -176,7 +180,7 @@ def _model_block(enc, b, dec_t, lut):
     return ((sm & 0x80) << 8) | (ex << 7) | (sm & 0x7F), any(bad)
 
 
-def _check(w, blocks=None):
+def _check(w, blocks=None, geo=NARROW):
     enc = hd.encode(w)
     lut = enc.luts.view(np.uint16)
     dec_t = _table(lut, enc.codebook.n_tables, enc.codebook.max_len)
@@ -184,9 +188,9 @@ def _check(w, blocks=None):
     fallbacks = 0
     for b in (range(nb) if blocks is None else blocks):
         p0, p1 = int(enc.block_pos[b]), int(enc.block_pos[b + 1])
-        if p1 - p0 > TILE_CAP - 16:
+        if p1 - p0 > geo["cap"] - 16:
             continue  # multi-pass blocks: checked on the GPU only
-        got, fell_back = _model_block(enc, b, dec_t, lut)
+        got, fell_back = _model_block(enc, b, dec_t, lut, geo)
         fallbacks += fell_back
         assert np.array_equal(got, w[p0:p1]), f"block {b}"
     return fallbacks
@@ -205,6 +209,20 @@ def test_model_fallback_on_short_codes():
     low = rng.integers(0, 256, e.size, dtype=np.uint16)
     w = (((low & 0x80) << 8) | (e << 7) | (low & 0x7F)).astype(np.uint16)
     assert _check(w) > 0
+
+
+@pytest.mark.parametrize("kind,n,seed", [("geometric", 30_000, 21), ("geometric_steep", 30_000, 22),
+                                          ("normal", 9000, 23)])
+def test_model_wide_slots(kind, n, seed):
+    """The 56-code slots: streams of 1.4-2 bit codes (30-45 codes per slice)
+    stage every block that the 32-code slots send to the fallback, and
+    ordinary weights decode the same way in either geometry."""
+    w = wl.random_small(n, seed, kind)
+    wide = _check(w, geo=WIDE)
+    if kind == "geometric":
+        assert _check(w) > 0 and wide == 0
+    if kind == "normal":
+        assert wide == 0
 
 
 def test_model_all_exponents():
