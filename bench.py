@@ -804,31 +804,38 @@ def main() -> int:
     }
     if not args.no_gemm:
         line["decode_vs_gemm"] = gemm_ratios(wlx, out, avg_ms, stream)
-        # the fused product (df11_decode_gemv at batch 1, df11_decode_gemm at
-        # 2 and 4) against the BF16 GEMMs on resident weights and against
-        # decoding first and then running those GEMMs
-        fused = {}
+        # The fused products against the BF16 GEMMs on resident weights and
+        # against decoding first and then running those GEMMs:
+        #   fused: the library's product for 1-64 vectors on the matrix cores
+        #     (df11_decode_gemm_tiled), from the block encoded in operand-tile
+        #     order (the same code book and compressed size);
+        #   fused_row_major: the product on the row-major stream itself
+        #     (df11_decode_gemv at batch 1, df11_decode_gemm at 2 and 4).
+        # The bytes a fused product must move: the compressed weights, x (bf16)
+        # and y (fp32).
         nx = sum(m.cols for m in wlx.matrices)
         ny = sum(m.rows for m in wlx.matrices)
-        for b in (1, 2, 4):
-            f = fused_gemv(wlx, copies, stream) if b == 1 else fused_gemm(wlx, copies, stream, b)
+
+        def priced(f, b):
             g = line["decode_vs_gemm"][f"batch{b}"]["gemm_ms"]
             f["over_bf16_gemm"] = round(f["fused_ms"] / g, 4)
             f["over_decode_then_gemm"] = round(f["fused_ms"] / (avg_ms + g), 4)
-            # the bytes a fused product must move: the compressed weights, x
-            # (bf16) and y (fp32)
             f["fused_gbs"] = round((rd + 2 * b * nx + 4 * b * ny) / (f["fused_ms"] * 1e-3) / 1e9, 1)
-            fused[f"batch{b}"] = f
-        line["decode_vs_gemm"]["fused"] = fused
-        # the tiled product on the matrix cores (its own tile-order encoding)
+            return f
+
         tiled = fused_tiled(wlx, stream, (1, 2, 4, 16, 64))
+        tile_decode = tiled.pop("decode_row_major")
+        fused = {"path": "df11_decode_gemm_tiled (operand-tile-order stream)"}
         for key, f in tiled.items():
-            if not key.startswith("batch"):  # the row-major decode of the same stream
-                continue
-            g = line["decode_vs_gemm"][key]["gemm_ms"]
-            f["over_bf16_gemm"] = round(f["fused_ms"] / g, 4)
-            f["over_decode_then_gemm"] = round(f["fused_ms"] / (avg_ms + g), 4)
-        line["decode_vs_gemm"]["fused_tiled"] = tiled
+            fused[key] = priced(f, int(key[len("batch"):]))
+        line["decode_vs_gemm"]["fused"] = fused
+        row_major = {"path": "df11_decode_gemv / df11_decode_gemm (row-major stream)"}
+        for b in (1, 2, 4):
+            f = fused_gemv(wlx, copies, stream) if b == 1 else fused_gemm(wlx, copies, stream, b)
+            row_major[f"batch{b}"] = priced(f, b)
+        line["decode_vs_gemm"]["fused_row_major"] = row_major
+        # the tile-order stream decoded back to row-major BF16 (df11_decode_tiled)
+        line["decode_vs_gemm"]["tile_order_decode"] = {"path": "df11_decode_tiled", **tile_decode}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wlx, enc)
     print(json.dumps(line), flush=True)
