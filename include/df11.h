@@ -108,7 +108,9 @@ int df11_build_luts(const df11_codebook *cb, void *lut, uint64_t lut_cap);
 typedef struct df11_sizes {
     uint64_t n;
     uint64_t total_bits;
-    uint64_t last_start;       /* first bit of the final code */
+    uint64_t last_start;       /* first bit of the final code (df11_encode
+                                  fills it; df11_encoded_sizes cannot and
+                                  leaves 0) */
     uint64_t stream_bytes;     /* n_blocks * 512 + DF11_STREAM_GUARD */
     uint64_t gaps_bytes;       /* 40 * n_blocks + 8 (5-bit fields, dword padded) */
     uint64_t block_pos_count;  /* n_blocks + 1 */
@@ -122,6 +124,8 @@ typedef struct df11_sizes {
  * into 8-byte per-thread slices, one Gaps field per slice and one
  * BlockOutputPos entry per block; section "How it works": the stream holds
  * sum over symbols of count x code length bits), from the histogram alone.
+ * last_start depends on the order of the weights and is left 0: take it,
+ * with the rest of the sizes, from df11_encode's output.
  * Errors: ARG, FORMAT (hist does not sum to n or holds a symbol without a
  * code). */
 int df11_encoded_sizes(const uint64_t hist[256], uint64_t n, const df11_codebook *cb,

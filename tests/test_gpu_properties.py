@@ -1,7 +1,9 @@
 """Property tests on the GPU: generated inputs through df11_decode (the
 result must be the original words, bit for bit) and generated matrix lists
 and batches through the tiled product in its exact mode (every sum must
-equal numpy's fp64 product bit for bit).  Each case prints what it runs."""
+equal numpy's fp64 product bit for bit), and generated matrix lists through
+the tile-order encoding and its decode back to row-major (bit for bit).  Each
+case prints what it runs."""
 import numpy as np
 import pytest
 
@@ -55,3 +57,16 @@ def test_tiled_generated_shapes_exact(torch, shapes, batch, seed, kind):
     big = ((w >> 7) & 0xFF) > e_max
     w[big] = (w[big] & 0x807F) | np.uint16(e_max << 7)
     _check(torch, w, shapes, batch, f"generated {shapes} {kind}", exact=True, seed=seed)
+
+
+@settings(max_examples=20, **_SETTINGS)
+@given(shapes=matrix_lists(), seed=st.integers(0, 10_000),
+       kind=st.sampled_from(["normal", "single", "uniform", "geometric"]))
+def test_decode_tiled_generated_shapes(torch, shapes, seed, kind):
+    """Generated matrix lists through the tile-order encoding and back: the
+    decode to row-major must give the original words bit for bit."""
+    from huffman_decode_amd import workloads as wl
+    from test_gpu_decode_tiled import _decode_tiled
+    w = wl.random_small(sum(r * c for r, c in shapes), seed, kind)
+    te = hd.encode_tiled(w, shapes)
+    assert np.array_equal(_decode_tiled(torch, te, f"generated {shapes} {kind}"), w)
