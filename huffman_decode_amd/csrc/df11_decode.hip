@@ -65,19 +65,22 @@ constexpr int kMaxBlockCodes = DF11_BLOCK_SLICES * DF11_SLICE_BITS;  // all 1-bi
 // LDS region (the 4 bytes in front let every lane read the dword before its
 // slot); a lane with more than kCodes codes, or with fewer than 3 before the
 // block's last code, sends the wave to the re-decode route.  The tile that
-// phase 2 fills reuses the region.  32 codes per lane serve every stream of
-// ordinary weights (about 24 codes of 2.6 bits per 64-bit slice); streams of
-// much shorter codes get 56, with a larger region and fewer workgroups per
-// CU.
+// phase 2 fills reuses the region.  32 codes per lane (40-byte slots) serve
+// every stream of ordinary weights (about 24 codes of 2.6 bits per 64-bit
+// slice); streams of much shorter codes get 56 codes per lane in 60-byte
+// slots, with a larger region and fewer workgroups per CU.  (The odd stride
+// of 15 dwords starts consecutive lanes' slots on distinct LDS banks; with
+// 64-byte slots they start on a few banks, and their conflicts cost the wide
+// kernel a quarter of its speed.)
 constexpr int kStageBase = 4;
 constexpr int kStageMinCodes = 3;
 // phase 1 writes at most 71 bytes from a slot's start, whatever the data: a
 // step begins below bit 64 and every code takes at least one bit, so the
 // last step begins after at most 63 codes and stores two aligned dwords
 constexpr int kStageReach = 63 + 8;
-template <int kCodes> struct StageGeo {
+template <int kCodes, int kStride> struct StageGeo {
     static constexpr int kStageCodes = kCodes;
-    static constexpr int kStageStride = kCodes + 8;
+    static constexpr int kStageStride = kStride;
     // the wave's region: all 64 slots, 8-aligned
     static constexpr int kTileBytes = (kStageBase + 63 * kStageStride + kStageReach + 7) / 8 * 8;
     // exponent bytes one tile holds; blocks with more symbols take several passes
@@ -89,8 +92,10 @@ template <int kCodes> struct StageGeo {
     static_assert(kCodes % 4 == 0, "slots move in whole dwords");
     static_assert(kTilesBytes < 0x10000, "tile addresses must fit 16 bits");
 };
-using NarrowGeo = StageGeo<32>;
-using WideGeo = StageGeo<56>;
+using NarrowGeo = StageGeo<32, 40>;
+using WideGeo = StageGeo<56, 60>;
+template <int kCodes>
+using GeoFor = typename std::conditional<kCodes == NarrowGeo::kStageCodes, NarrowGeo, WideGeo>::type;
 constexpr int kStageStride = NarrowGeo::kStageStride;
 constexpr int kStageCodes = NarrowGeo::kStageCodes;
 constexpr int kTileCap = NarrowGeo::kTileCap;
@@ -1109,7 +1114,7 @@ __device__ __forceinline__ void decode_blocks(const DecodeArgs &a, Sink &sink) {
 template <int kCodes>
 __global__ __launch_bounds__(kGroupThreads) DF11_OCCUPANCY_HINT void df11_decode_kernel(DecodeArgs a) {
     StoreSink sink{a.out};
-    decode_blocks<StageGeo<kCodes>>(a, sink);
+    decode_blocks<GeoFor<kCodes>>(a, sink);
 }
 
 // The decode of a tile-order stream into row-major words.  Thread 0 copies
@@ -1869,15 +1874,14 @@ int launch_groups(K kernel, int which, int dev, uint32_t n_tables, uint32_t n_bl
 }
 
 // The plain decode stages up to 56 codes per lane (instead of 32) for a
-// stream whose codes average under 64 / 30 = 2.13 bits: 30 or more codes
-// start in a 64-bit slice, and nearly every block holds a lane with more than
-// 32 (ordinary BF16 weights average 2.6-2.8 bits, 23-25 codes per slice).
-// The wider slots cost a workgroup per CU (3 instead of 4), which outweighs
-// the re-decode route for streams a little above 25 codes per slice: that
-// route is the cheaper of the two there.  Either kernel decodes every stream;
+// stream whose codes average under 64 / 25.5 = 2.51 bits: about 26 or more
+// codes start in a 64-bit slice, and most blocks hold a lane with more than
+// 32, which would send them to the re-decode route (ordinary BF16 weights
+// average 2.6-2.8 bits, 23-25 codes per slice, and keep the 32-code slots
+// and their extra workgroup per CU).  Either kernel decodes every stream;
 // the choice only decides which blocks take the re-decode route.
 bool uses_wide_slots(const df11_device_stream *s) {
-    return 64 * (unsigned __int128)s->n > 30 * (unsigned __int128)s->total_bits;
+    return 128 * (unsigned __int128)s->n > 51 * (unsigned __int128)s->total_bits;
 }
 
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }

@@ -180,7 +180,7 @@ typedef struct df11_device_stream {
  * exponents move to an LDS tile at those positions (blocks whose lanes hold
  * more than 32 or, short of the block's end, fewer than 3 codes instead
  * decode their slices a second time straight into the tile, the page's own
- * route; a stream whose codes average under 2.13 bits runs with slots of 56
+ * route; a stream whose codes average under 2.51 bits runs with slots of 56
  * codes instead of 32); each exponent is joined with its sign|mantissa byte and the
  * words are written with coalesced 16-byte stores.  Enqueued on hip_stream
  * (a hipStream_t; NULL = the null stream) and returns without waiting.  out

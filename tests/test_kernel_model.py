@@ -30,9 +30,9 @@ MIN_CODES = 3          # fewer (before the block's last code) also does
 # staging geometries: codes a lane may stage (more sends the wave to the
 # fallback), bytes of staging per lane, LDS bytes per wave (staging and tile
 # share them), exponent bytes one tile holds.  The kernel stages 32 codes per
-# lane, and 56 for streams whose codes average under 2.13 bits.
+# lane, and 56 for streams whose codes average under 2.51 bits.
 NARROW = dict(codes=32, stride=40, region=2600, cap=2560)
-WIDE = dict(codes=56, stride=64, region=4112, cap=4072)
+WIDE = dict(codes=56, stride=60, region=3856, cap=3816)
 TILE_CAP = NARROW["cap"]
 STRAY = 0xEE           # value of the unfilled slots of a decode entry in this model
 
