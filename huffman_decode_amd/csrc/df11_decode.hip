@@ -1934,14 +1934,17 @@ extern "C" int df11_decode(const df11_device_stream *s, uint16_t *out, void *hip
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return DF11_ERR_HIP;
     int groups = 0;
-    if (uses_wide_slots(s)) {
-        st = launch_groups(df11_decode_kernel<WideGeo::kStageCodes>, 6, dev, s->n_tables,
-                           s->n_blocks, s->max_groups, &groups);
-        if (st != DF11_OK) return st;
+    // (the wide kernel's LDS is 10 KB larger: with a table hierarchy that
+    // leaves it no room, the narrow one decodes the stream)
+    st = uses_wide_slots(s) ? launch_groups(df11_decode_kernel<WideGeo::kStageCodes>, 6, dev,
+                                            s->n_tables, s->n_blocks, s->max_groups, &groups)
+                            : DF11_ERR_TABLES;
+    if (st == DF11_OK) {
         hipLaunchKernelGGL(df11_decode_kernel<WideGeo::kStageCodes>, dim3(groups),
                            dim3(kGroupThreads), lds_bytes(s->n_tables),
                            static_cast<hipStream_t>(hip_stream), a);
     } else {
+        if (st != DF11_ERR_TABLES) return st;
         st = launch_groups(df11_decode_kernel<NarrowGeo::kStageCodes>, 0, dev, s->n_tables,
                            s->n_blocks, s->max_groups, &groups);
         if (st != DF11_OK) return st;
