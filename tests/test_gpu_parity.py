@@ -298,6 +298,43 @@ def _oracle_blocks(enc, fetch, blocks):
         assert np.array_equal(fetch(p0, p1), oracle.join_bf16(ex, enc.signmant[p0:p1])), f"block {b}"
 
 
+def test_decode_at_the_largest_n(torch):
+    """The largest stream the format's 32-bit output positions allow, to the
+    nearest multiple of 64: n = 2^32 - 64 words (8.6 GB of BF16, 64 copies of
+    one 2^26 - 1-word N(0, 0.02) draw, seed 77).  Every output position, block
+    index and stream offset of the kernel is then at its widest.  The decode
+    must give the original words bit for bit, leave the guard past n alone and
+    report no block; the oracle decodes the first and the last two blocks on
+    its own."""
+    chunk = wl.random_small((1 << 26) - 1, 77, "normal")
+    n = 64 * chunk.size
+    assert n == (1 << 32) - 64
+    _say(f"[gpu] df11_decode largest n={n}: encoding")
+    w = np.tile(chunk, 64)
+    enc = hd.encode(w)
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    dev = hd.to_device(enc, status=st)
+    out = torch.full((n + GUARD,), 0x5555, dtype=torch.int16, device="cuda")
+    _say(f"[gpu] df11_decode largest n={n} blocks={enc.sizes.n_blocks} "
+         f"total_bits={enc.sizes.total_bits}: decoding")
+    hd.df11_decode(dev, out)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    assert bool((out[n:] == 0x5555).all()), "write past the end of the tensor"
+    ref = torch.from_numpy(w.view(np.int16)).cuda()
+    assert torch.equal(out[:n], ref), "decoded words differ from the originals"
+    del ref
+    nb = int(enc.sizes.n_blocks)
+    stop = int(enc.sizes.last_start) + 1
+    for b in (0, nb - 2, nb - 1):
+        p0, p1 = int(enc.block_pos[b]), int(enc.block_pos[b + 1])
+        gap = int(enc.gaps[40 * b]) & 31  # block b's first 5-bit field starts at byte 40 b
+        ex = oracle.decode_range(enc.stream, int(enc.sizes.total_bits), 4096 * b + gap,
+                                 min(4096 * (b + 1), stop), enc.codebook.lengths, 4096)
+        got = out[p0:p1].cpu().numpy().view(np.uint16)
+        assert np.array_equal(got, oracle.join_bf16(ex, enc.signmant[p0:p1])), f"block {b}"
+
+
 @pytest.mark.parametrize("layer", list(range(32)))
 def test_stack_block_full_size(torch, layer):
     """The 32-block Llama-3.1-8B-shaped stack at full size, one block at a

@@ -204,6 +204,53 @@ def test_tiled_llama8b_block_full(torch, batch):
            exact=False)
 
 
+def test_tiled_paths_at_the_largest_n(torch):
+    """One 262,080 x 16,384 matrix: n = 4,293,918,720 words, within 2^20 of
+    the format's 32-bit limit, and 8,386,560 operand tiles (the tile-order
+    decode divides tile indices by a float reciprocal, exact below 2^23).
+    The weights repeat one seeded draw of 64 rows (|w| in [2^-8, 2^-5) or 0,
+    so each row's sum of |w| stays below 2^9).  The tiled product at one and
+    at 64 vectors in {-1, 0, 1} must equal numpy's fp64 product bit for bit
+    on sampled rows (every 64-row period, first and last rows included), and
+    the tile-order decode must give back every word."""
+    rows, cols = 262_080, 16_384
+    chunk = _exact_weights(64 * cols, 91)
+    big = ((chunk >> 7) & 0xFF) >= 127 - 5
+    chunk[big] = (chunk[big] & 0x807F) | np.uint16((127 - 6) << 7)
+    w = np.tile(chunk, rows // 64)
+    n = w.size
+    assert n == rows * cols and (1 << 32) - n <= (1 << 20)
+    _say(f"[gpu] tiled paths largest n={n}: encoding")
+    te = hd.encode_tiled(w, [(rows, cols)])
+    td = hd.tiled_to_device(te)
+    wc = _bf16_to_f64(torch, chunk).reshape(64, cols)
+    sample = np.unique(np.concatenate([np.arange(64), rows - 64 + np.arange(64),
+                                       np.random.default_rng(92).integers(0, rows, 256)]))
+    for batch in (1, 64):
+        x_bits = np.array([0xBF80, 0, 0x3F80], np.uint16)[
+            np.random.default_rng(93 + batch).integers(0, 3, (batch, cols))]
+        x = torch.from_numpy(x_bits.view(np.int16)).cuda().view(torch.bfloat16)
+        need = hd.df11_tiled_workspace_bytes(te.mats, batch)
+        ws = torch.empty(need, dtype=torch.uint8, device="cuda") if need else None
+        y = torch.full((batch, rows + 5), -7.0, dtype=torch.float32, device="cuda")
+        _say(f"[gpu] df11_decode_gemm_tiled largest n={n} batch={batch}")
+        hd.df11_decode_gemm_tiled(td, x, y[:, :rows], ws)
+        torch.cuda.synchronize()
+        h = y.cpu().numpy()
+        assert np.all(h[:, rows:] == -7.0), "wrote past the results"
+        xf = _bf16_to_f64(torch, x_bits)
+        ref = xf @ wc.T  # [batch, 64]: row r of the matrix is chunk row r % 64
+        assert (np.abs(xf) @ np.abs(wc).T).max() < 2.0 ** 9
+        got = h[:, sample].astype(np.float64)
+        assert np.array_equal(got, ref[:, sample % 64]), f"batch {batch}"
+    out = torch.full((n + 40,), 0x5555, dtype=torch.int16, device="cuda")
+    _say(f"[gpu] df11_decode_tiled largest n={n}")
+    hd.df11_decode_tiled(td, out)
+    torch.cuda.synchronize()
+    assert bool((out[n:] == 0x5555).all()), "write past the end of the tensor"
+    assert torch.equal(out[:n], torch.from_numpy(w.view(np.int16)).cuda())
+
+
 @pytest.mark.parametrize("batch", [1, 8])
 def test_tiled_corrupt_blocks_stay_contained(torch, batch):
     """Flipped stream bits: the blocks whose counts no longer match are
