@@ -335,6 +335,50 @@ def test_decode_at_the_largest_n(torch):
         assert np.array_equal(got, oracle.join_bf16(ex, enc.signmant[p0:p1])), f"block {b}"
 
 
+def test_fused_products_at_the_largest_n(torch):
+    """The row-major fused products on one 262,080 x 16,384 matrix (n within
+    2^20 of the format's 32-bit limit; 64 rows of one seeded draw repeated,
+    |w| in [2^-8, 2^-5) or 0) with inputs in {-1, 0, 1}: every partial sum is
+    a multiple of 2^-15 below 2^9, exact in fp32 in any order, so df11_decode_gemv
+    and df11_decode_gemm (8 vectors) must equal numpy's fp64 product bit for
+    bit on sampled rows, and write nothing past the results."""
+    rows, cols = 262_080, 16_384
+    chunk = wl.random_small(64 * cols, 94, "normal").copy()
+    e = (chunk >> 7) & 0xFF
+    chunk[e < 127 - 8] = 0
+    chunk[e >= 127 - 5] = (chunk[e >= 127 - 5] & 0x807F) | np.uint16((127 - 6) << 7)
+    w = np.tile(chunk, rows // 64)
+    n = w.size
+    _say(f"[gpu] fused products largest n={n}: encoding")
+    enc = hd.encode(w)
+    dev = hd.to_device(enc)
+    mats, nx, ny = hd.gemv_matrices([(rows, cols)])
+    wc = torch.from_numpy(chunk.view(np.int16)).view(torch.bfloat16).double().numpy().reshape(64, cols)
+    sample = np.unique(np.concatenate([np.arange(64), rows - 64 + np.arange(64),
+                                       np.random.default_rng(95).integers(0, rows, 256)]))
+    for batch in (1, 8):
+        x_bits = np.array([0xBF80, 0, 0x3F80], np.uint16)[
+            np.random.default_rng(96 + batch).integers(0, 3, (batch, nx))]
+        x = torch.from_numpy(x_bits.view(np.int16)).cuda().view(torch.bfloat16)
+        y = torch.full((batch, ny + 5), -7.0, dtype=torch.float32, device="cuda")
+        _say(f"[gpu] fused products largest n={n} batch={batch}")
+        if batch == 1:
+            ws = torch.empty(hd.df11_gemv_workspace_bytes(dev), dtype=torch.uint8, device="cuda")
+            hd.df11_decode_gemv(dev, mats, x[0], y[0], ws)
+        else:
+            ws = torch.empty(hd.df11_gemm_workspace_bytes(dev, batch), dtype=torch.uint8,
+                             device="cuda")
+            hd.df11_decode_gemm(dev, mats, x, y[:, :ny], ws)
+        torch.cuda.synchronize()
+        h = y.cpu().numpy()
+        assert np.all(h[:, ny:] == -7.0), "wrote past the results"
+        xf = torch.from_numpy(x_bits.view(np.int16)).view(torch.bfloat16).double().numpy()
+        assert (np.abs(xf) @ np.abs(wc).T).max() < 2.0 ** 9
+        ref = (xf @ wc.T)[:, sample % 64]
+        assert np.array_equal(h[:, sample].astype(np.float64), ref), f"batch {batch}"
+        del ws
+
+
 @pytest.mark.parametrize("layer", list(range(32)))
 def test_stack_block_full_size(torch, layer):
     """The 32-block Llama-3.1-8B-shaped stack at full size, one block at a
