@@ -68,7 +68,7 @@ constexpr int kMaxBlockCodes = DF11_BLOCK_SLICES * DF11_SLICE_BITS;  // all 1-bi
 // phase 2 fills reuses the region.  32 codes per lane (40-byte slots) serve
 // every stream of ordinary weights (about 24 codes of 2.6 bits per 64-bit
 // slice); streams of much shorter codes get 56 codes per lane in 60-byte
-// slots, with a larger region and fewer workgroups per CU.  (The odd stride
+// slots, in a larger region (both run 3 workgroups per CU).  (The odd stride
 // of 15 dwords starts consecutive lanes' slots on distinct LDS banks; with
 // 64-byte slots they start on a few banks, and their conflicts cost the wide
 // kernel a quarter of its speed.)
@@ -1877,9 +1877,10 @@ int launch_groups(K kernel, int which, int dev, uint32_t n_tables, uint32_t n_bl
 // stream whose codes average under 64 / 25.5 = 2.51 bits: about 26 or more
 // codes start in a 64-bit slice, and most blocks hold a lane with more than
 // 32, which would send them to the re-decode route (ordinary BF16 weights
-// average 2.6-2.8 bits, 23-25 codes per slice, and keep the 32-code slots
-// and their extra workgroup per CU).  Either kernel decodes every stream;
-// the choice only decides which blocks take the re-decode route.
+// average 2.6-2.8 bits, 23-25 codes per slice, decode as fast with either,
+// and keep the 32-code slots, whose LDS leaves more room for the tables).
+// Either kernel decodes every stream; the choice only decides which blocks
+// take the re-decode route.
 bool uses_wide_slots(const df11_device_stream *s) {
     return 128 * (unsigned __int128)s->n > 51 * (unsigned __int128)s->total_bits;
 }
