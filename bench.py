@@ -826,6 +826,7 @@ def main() -> int:
             f["over_bf16_bytes_at_peak"] = round(
                 f["fused_ms"] / line["decode_vs_gemm"][f"batch{b}"]["bf16_bytes_at_peak_ms"], 4)
             f["fused_gbs"] = round((rd + 2 * b * nx + 4 * b * ny) / (f["fused_ms"] * 1e-3) / 1e9, 1)
+            f["frac_of_hbm_peak"] = round(f["fused_gbs"] / HBM_PEAK_GBS, 4)
             return f
 
         tiled = fused_tiled(wlx, stream, (1, 2, 4, 16, 64))
