@@ -58,7 +58,9 @@ extern "C" {
 #define DF11_BLOCK_BYTES 512
 #define DF11_STREAM_GUARD 16
 #define DF11_MAX_TABLES 64
-#define DF11_MAX_N 0xFFFFFFFFull /* n must be below 2^32: block_pos is uint32 */
+/* Largest n: 2^32 - 64.  block_pos is uint32, and the kernels form output
+ * positions up to a block's end plus one 8-word group in 32 bits. */
+#define DF11_MAX_N 0xFFFFFFC0ull
 
 enum {
     DF11_OK = 0,

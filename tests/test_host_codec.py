@@ -514,3 +514,22 @@ def test_decode_tiled_refuses_bad_matrix_lists_before_any_device_call():
     assert call(gap, 2) == -1                                    # not end to end
     many = hd.gemv_matrices([(16, 32)] * 17)[0]
     assert call(many, 17) == -1                                  # more than 16
+
+
+def test_largest_n_is_accepted_and_one_more_is_refused():
+    """n up to 2^32 - 64 passes the size and descriptor checks; 2^32 - 63 is
+    refused by both (the kernels' 32-bit positions need a group of headroom)."""
+    lib = hd.library()
+    top = (1 << 32) - 64
+    for n, want in ((top, 0), (top + 1, -1)):
+        hist = np.zeros(256, np.uint64)
+        hist[127] = n
+        cb = hd.Codebook()
+        assert lib.df11_build_codebook(hist.ctypes.data, 32, ctypes.byref(cb)) == 0
+        sz = hd.Sizes()
+        assert lib.df11_encoded_sizes(hist.ctypes.data, n, ctypes.byref(cb), ctypes.byref(sz)) == want
+    d = hd.DeviceStream()
+    fake = 1 << 20
+    d.stream = d.gaps = d.block_pos = d.signmant = d.luts = fake
+    d.n = top + 1
+    assert lib.df11_decode(ctypes.byref(d), fake, None) == -1
