@@ -1792,7 +1792,10 @@ void df11_tiled_kernel(DecodeArgs a, TiledArgs t) {
                 decode_codes<true>(lds_dec, lut, a.n_tables, cur.d0, cur.d1, cur.d2, start, lim,
                                    tile_addr, at, r0);
                 wave_lds_sync();
-                const uint32_t r_lo = base + r0, r_hi = base + r0 + kTileCap;
+                // (the window's end clamped to the block's, so that it cannot
+                // pass 2^32 at the end of the largest stream)
+                const uint32_t r_lo = base + r0, room = p1 > r_lo ? p1 - r_lo : 0u;
+                const uint32_t r_hi = r_lo + (room < (uint32_t)kTileCap ? room : (uint32_t)kTileCap);
                 const uint32_t v_lo = w_lo > r_lo ? w_lo : r_lo, v_hi = w_hi < r_hi ? w_hi : r_hi;
                 if (v_lo < v_hi)
                     mfma_window<NT, kX1>(v_lo, v_lo, v_hi, false, r_lo, tile, a.signmant, xs, seg_tile,
