@@ -298,6 +298,37 @@ def _oracle_blocks(enc, fetch, blocks):
         assert np.array_equal(fetch(p0, p1), oracle.join_bf16(ex, enc.signmant[p0:p1])), f"block {b}"
 
 
+def _skewed_stream(k, seed, total=1 << 21):
+    """Exponent j < k with count total / 2^(j+1), every other exponent 1-3
+    times, shuffled, random sign|mantissa: short codes for the common
+    exponents (about 2 bits on average) and many long ones under different
+    8-bit prefixes, so the code book needs many lookup tables."""
+    rng = np.random.default_rng(seed)
+    h = np.zeros(256, np.int64)
+    for j in range(k):
+        h[j] = max(1, total >> (j + 1))
+    h[k:] = rng.integers(1, 4, 256 - k)
+    e = np.repeat(np.arange(256, dtype=np.uint16), h)
+    np.random.default_rng(seed + 1000).shuffle(e)
+    low = np.random.default_rng(seed + 2000).integers(0, 256, e.size).astype(np.uint16)
+    return (((low & 0x80) << 8) | (e << 7) | (low & 0x7F)).astype(np.uint16)
+
+
+@pytest.mark.parametrize("k,seed,tables", [(4, 0, 17), (8, 4, 38), (8, 156, 53)])
+def test_many_lookup_tables(torch, k, seed, tables):
+    """Code books of 17, 38 and 53 8-bit tables (up to 27 KB of them in LDS
+    beside the decode table and the staging regions; the codes average under
+    2.51 bits, so the wide-slot kernel runs): bit-exact, and sampled blocks
+    decoded by the oracle on their own."""
+    w = _skewed_stream(k, seed)
+    enc = hd.encode(w)
+    assert enc.codebook.n_tables == tables
+    got = _gpu_decode(torch, enc, f"tables={tables}")
+    assert np.array_equal(got, w)
+    nb = int(enc.sizes.n_blocks)
+    _oracle_blocks(enc, lambda p0, p1: got[p0:p1], sorted({0, nb // 2, nb - 1}))
+
+
 def test_decode_at_the_largest_n(torch):
     """The largest stream the format's 32-bit output positions allow, to the
     nearest multiple of 64: n = 2^32 - 64 words (8.6 GB of BF16, 64 copies of
