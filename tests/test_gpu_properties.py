@@ -47,7 +47,7 @@ def matrix_lists(draw):
 
 @settings(max_examples=25, **_SETTINGS)
 @given(shapes=matrix_lists(), batch=st.integers(1, 64), seed=st.integers(0, 10_000),
-       kind=st.sampled_from(["normal", "single"]))
+       kind=st.sampled_from(["normal", "single", "geometric"]))
 def test_tiled_generated_shapes_exact(torch, shapes, batch, seed, kind):
     w = _exact_weights(sum(r * c for r, c in shapes), seed, kind)
     # keep every row's sum of |w| below 2^9: |w| < 2^(e - 126) for exponent
