@@ -13,7 +13,12 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 EXE = os.path.join(HERE, "c_abi", "df11_roundtrip")
 
 
-def _run(*args, timeout=120):
+def _run(*args, timeout=120, build_if_missing=False):
+    if not os.path.exists(EXE) and build_if_missing:  # the host half only: a CPU compile
+        import sys
+        sys.path.insert(0, os.path.dirname(HERE))
+        from tests.c_abi.build import build_roundtrip
+        build_roundtrip()
     if not os.path.exists(EXE):
         pytest.fail(f"{EXE} is missing: build it with __graft_entry__.build()")
     print(f"[c_abi] df11_roundtrip {' '.join(args)}", flush=True)
@@ -22,7 +27,7 @@ def _run(*args, timeout=120):
 
 @pytest.mark.parametrize("n,seed", [(1, 1), (65, 2), (200_003, 5)])
 def test_c_program_host_half(n, seed):
-    r = _run("--host", str(n), str(seed))
+    r = _run("--host", str(n), str(seed), build_if_missing=True)
     assert r.returncode == 0, r.stdout + r.stderr
     assert "df11_roundtrip host ok" in r.stdout
 
