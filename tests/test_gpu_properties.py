@@ -30,7 +30,7 @@ def torch():
     return t
 
 
-@settings(max_examples=40, **_SETTINGS)
+@settings(max_examples=100, **_SETTINGS)
 @given(w=bf16_words(max_n=200_000), cap=st.integers(20, 32))
 def test_decode_generated_inputs(torch, w, cap):
     enc = hd.encode(w, max_code_len=cap)
@@ -45,7 +45,7 @@ def matrix_lists(draw):
     return shapes
 
 
-@settings(max_examples=25, **_SETTINGS)
+@settings(max_examples=60, **_SETTINGS)
 @given(shapes=matrix_lists(), batch=st.integers(1, 64), seed=st.integers(0, 10_000),
        kind=st.sampled_from(["normal", "single", "geometric"]))
 def test_tiled_generated_shapes_exact(torch, shapes, batch, seed, kind):
@@ -59,7 +59,7 @@ def test_tiled_generated_shapes_exact(torch, shapes, batch, seed, kind):
     _check(torch, w, shapes, batch, f"generated {shapes} {kind}", exact=True, seed=seed)
 
 
-@settings(max_examples=20, **_SETTINGS)
+@settings(max_examples=50, **_SETTINGS)
 @given(shapes=matrix_lists(), seed=st.integers(0, 10_000),
        kind=st.sampled_from(["normal", "single", "uniform", "geometric"]))
 def test_decode_tiled_generated_shapes(torch, shapes, seed, kind):

@@ -16,7 +16,7 @@ import oracle  # noqa: E402
 from gen_words import bf16_words  # noqa: E402
 
 
-@settings(max_examples=300, deadline=None, database=None, derandomize=True)
+@settings(max_examples=600, deadline=None, database=None, derandomize=True)
 @given(w=bf16_words(), slack=st.integers(0, 31))
 def test_encoder_output_decodes_back_and_matches_the_oracle(w, slack):
     e, _ = oracle.split_bf16(w)
