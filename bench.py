@@ -763,6 +763,22 @@ def main() -> int:
     bit_exact = all(bool(torch.equal(o.view(torch.int16), orig)) for o in written)
     del orig
     traffic = measured_traffic(rd + wr)
+    # single launches, each between its own pair of events (after the timed
+    # region; the events add gaps between launches, so these give the spread,
+    # while `value` comes from the back-to-back mean above)
+    singles = []
+    for k in range(20):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        decode(k)
+        b.record(stream)
+        singles.append((a, b))
+    torch.cuda.synchronize()
+    singles = sorted(a.elapsed_time(b) for a, b in singles)
+    # the exponent histogram's entropy: the floor of the average code length
+    hist = hd.df11_histogram(wlx.weights).astype(np.float64)
+    prob = hist[hist > 0] / hist.sum()
+    entropy = float(-(prob * np.log2(prob)).sum())
     # the ceiling, timed right after the decode on the same copies and buffers
     c_ms, _ = timed(ceiling, args.steps, 20)
     ceiling_gbs = (n8 + b_bytes + 2 * n8) / (c_ms * 1e-3) / 1e9
@@ -786,12 +802,18 @@ def main() -> int:
         "data": "synthetic",
         "gweights_per_s": round(n / (avg_ms * 1e-3) / 1e9, 2),
         "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
-        "kernel_ms": {"mean": round(avg_ms, 5)},
+        "kernel_ms": {"mean": round(avg_ms, 5),
+                      "single_launches": {"count": len(singles),
+                                          "median": round(singles[len(singles) // 2], 5),
+                                          "min": round(singles[0], 5),
+                                          "max": round(singles[-1], 5)}},
         "bit_exact": bit_exact,
         "config": {"workload": args.workload, "n_weights": n,
                    "matrices": [f"{m.name}:{m.rows}x{m.cols}" for m in wlx.matrices],
                    "bits_per_weight": round(8 * (rd - int(enc.sizes.lut_bytes)) / n, 4),
                    "total_code_bits": int(enc.sizes.total_bits),
+                   "exponent_entropy_bits": round(entropy, 4),
+                   "avg_code_bits": round(int(enc.sizes.total_bits) / n, 4),
                    "max_code_len": int(enc.codebook.max_len),
                    "n_tables": int(enc.codebook.n_tables),
                    "rotating_copies": n_copies, "max_groups": args.max_groups,
