@@ -101,7 +101,9 @@ def cpu_baseline(wlx, enc) -> dict:
     """The oracle's bit-by-bit decode + join of the whole block: serially on one
     core, and split at block starts over the host's cores (each chunk of blocks
     decodes from its first slice's gap offset on its own, which is the chunk
-    decode property the DF11 format rests on).  Both are checked bit-exact."""
+    decode property the DF11 format rests on).  Both are checked bit-exact.
+    Beside them, the oracle's encoder on one core, checked against the arrays
+    of the product's host encoder."""
     import numpy as np
     from concurrent.futures import ThreadPoolExecutor
     import oracle
@@ -143,6 +145,19 @@ def cpu_baseline(wlx, enc) -> dict:
             runs.append(time.perf_counter() - t0)
             okn = okn and sizes_ok and bool(np.array_equal(out, wlx.weights))
     dtn = sorted(runs)[len(runs) // 2]
+
+    # the oracle's encoder on the whole block, one core: code book, bit-by-bit
+    # stream, gaps and block positions; it must give the arrays the product's
+    # host encoder gave
+    t0 = time.perf_counter()
+    oe = oracle.encode(wlx.weights)
+    dte = time.perf_counter() - t0
+    nbytes = (oe.total_bits + 7) // 8
+    enc_ok = (oe.total_bits == total and np.array_equal(oe.lengths, lengths)
+              and np.array_equal(oe.stream[:nbytes], enc.stream[:nbytes])
+              and np.array_equal(oe.block_pos, enc.block_pos[: oe.n_blocks + 1])
+              and np.array_equal(oe.signmant, enc.signmant[:n]))
+    del oe
     return {"value": round((rd + wr) / dtn / 1e9, 4), "unit": "GB/s", "cores": threads,
             "kind": "oracle", "gweights_per_s": round(n / dtn / 1e9, 5),
             "seconds": round(dtn, 3), "seconds_of_5_runs": [round(t, 3) for t in runs],
@@ -150,6 +165,8 @@ def cpu_baseline(wlx, enc) -> dict:
             "host_cpu_count": os.cpu_count(),
             "one_core": {"value": round((rd + wr) / dt1 / 1e9, 4), "unit": "GB/s", "cores": 1,
                          "gweights_per_s": round(n / dt1 / 1e9, 5), "seconds": round(dt1, 3)},
+            "encode_one_core": {"seconds": round(dte, 3), "gweights_per_s": round(n / dte / 1e9, 5),
+                                "same_arrays_as_host_encoder": bool(enc_ok)},
             "sample": f"whole {wlx.name} ({n} weights): oracle tree-walk decode of every "
                       f"code, then BF16 join; value: {len(edges) - 1} chunks of whole blocks "
                       f"on {threads} threads, median of 5 runs; one_core: serial from bit 0"}

@@ -1,6 +1,7 @@
 """bench.py's host-side parts, on the CPU: the refusal of more than one GPU,
 the algorithmic byte count behind `value` and `roofline.achieved`, and the
-CPU baseline leg (the oracle, bit-exact, with its core count)."""
+CPU baseline leg (the oracle, bit-exact, with its core count, and the
+oracle's encoder checked against the host encoder's arrays)."""
 import dataclasses
 import importlib.util
 import json
@@ -62,8 +63,10 @@ def test_cpu_baseline_is_the_oracle_and_checks_its_result():
     assert got["kind"] == "oracle" and got["bit_exact"] is True
     assert 1 <= got["cores"] <= 16 and got["one_core"]["cores"] == 1
     assert got["value"] > 0 and got["unit"] == "GB/s" and "small" in got["sample"]
+    assert got["encode_one_core"]["same_arrays_as_host_encoder"] is True
     # a flipped code bit must show: the check compares with the original words
     stream = enc.stream.copy()
     stream[len(stream) // 3] ^= np.uint8(0x10)
     bad = bench.cpu_baseline(wlx, dataclasses.replace(enc, stream=stream))
     assert bad["bit_exact"] is False
+    assert bad["encode_one_core"]["same_arrays_as_host_encoder"] is False
