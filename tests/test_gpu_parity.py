@@ -298,6 +298,24 @@ def _oracle_blocks(enc, fetch, blocks):
         assert np.array_equal(fetch(p0, p1), oracle.join_bf16(ex, enc.signmant[p0:p1])), f"block {b}"
 
 
+def test_every_gap_value_and_32_bit_codes(torch):
+    """A stream whose gap fields take all 32 values and whose code book has
+    32-bit codes (the Fibonacci histogram laid out so that codes end at every
+    offset 1..31 of a slice; 9.2 M words): bit-exact, and the blocks holding
+    the constructed codes decoded by the oracle on their own."""
+    import gap_streams as gs
+    hist = gs.fibonacci_hist()
+    lengths, _ = oracle.limited_lengths(hist, 32)
+    w = gs.every_gap_stream(lengths, hist)
+    enc = hd.encode(w)
+    nb = int(enc.sizes.n_blocks)
+    assert enc.codebook.max_len == 32
+    assert set(gs.gap_values(enc.gaps, 64 * nb + 1).tolist()) == set(range(32))
+    got = _gpu_decode(torch, enc, "every gap value")
+    assert np.array_equal(got, w)
+    _oracle_blocks(enc, lambda p0, p1: got[p0:p1], [0, 1, 2, nb - 1])
+
+
 def _skewed_stream(k, seed, total=1 << 21):
     """Exponent j < k with count total / 2^(j+1), every other exponent 1-3
     times, shuffled, random sign|mantissa: short codes for the common

@@ -533,3 +533,25 @@ def test_largest_n_is_accepted_and_one_more_is_refused():
     d.stream = d.gaps = d.block_pos = d.signmant = d.luts = fake
     d.n = top + 1
     assert lib.df11_decode(ctypes.byref(d), fake, None) == -1
+
+
+def test_constructed_stream_hits_every_gap_value_and_32_bit_codes():
+    """The Fibonacci histogram (codes up to 32 bits) laid out so that codes end
+    at every offset 1..31 of some slice: the host encoder's gap fields then take
+    all 32 values, and its arrays equal the oracle's, which decodes the stream
+    back to the words."""
+    import gap_streams as gs
+    hist = gs.fibonacci_hist()
+    lengths, _ = oracle.limited_lengths(hist, 32)
+    w = gs.every_gap_stream(lengths, hist)
+    enc = hd.encode(w)
+    assert enc.codebook.max_len == 32 and np.array_equal(enc.codebook.lengths, lengths)
+    nb, n, total = int(enc.sizes.n_blocks), int(enc.sizes.n), int(enc.sizes.total_bits)
+    g = gs.gap_values(enc.gaps, 64 * nb + 1)
+    assert set(g.tolist()) == set(range(32))
+    oe = oracle.encode(w)
+    nbytes = (total + 7) // 8
+    assert oe.total_bits == total and np.array_equal(oe.stream[:nbytes], enc.stream[:nbytes])
+    assert np.array_equal(oe.gaps, g) and np.array_equal(oe.block_pos, enc.block_pos[: nb + 1])
+    ex, end = oracle.decode(enc.stream, total, 0, n, lengths)
+    assert end == total and np.array_equal(oracle.join_bf16(ex, enc.signmant[:n]), w)
